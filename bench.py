@@ -1,0 +1,228 @@
+"""Decode-step benchmark on one MI355X.
+
+One step = the whole decode hot path for one batch: the slot of each
+sequence's newest token (pa_compute_slots), the write of its K/V into the
+pool (pa_cache_write), and paged attention over every context token
+(pa_decode, with its log-sum-exp merge pass when partitions split a context).
+
+Prints ONE JSON line.  ``value`` is context tokens per second (sum of
+context_lens over a step / step time) with every input already in HBM.
+``roofline`` rates the decode launch: algorithmic bytes (K and V of every
+context token, q, out, and the used block-table entries) over its mean
+duration, measured with HIP events on the stream the kernels run on, against
+the MI355X HBM peak of 8 TB/s.  ``cpu_baseline`` times the float64 oracle on
+a bounded sample of the same workload on this host.
+
+Pools are rotated between steps (several resident copies, each larger than
+the 256 MB last-level cache together with its neighbours), so a step never
+finds the previous step's K/V in cache.
+
+    python bench.py [--steps K] [--warmup W] [--config 1] [--partition-size P]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode: context tokens/s + achieved HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+ELEM = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def algorithmic_bytes(context_lens, num_heads, num_kv_heads, head_dim, block_size, dtype) -> dict:
+    """Bytes a decode launch must move at minimum: K and V rows of every
+    context token (per kv head), q and out (per query head) and the 4-byte
+    table entries in use.  Per token per kv head K+V is 2*D*e bytes, the
+    per-layer form of the KV size formula (2 x tokens x heads x head_dim x
+    element bytes)."""
+    e = ELEM[dtype]
+    ctx = [int(c) for c in context_lens]
+    kv = sum(ctx) * num_kv_heads * head_dim * e * 2
+    qo = 2 * len(ctx) * num_heads * head_dim * e
+    table = sum(-(-c // block_size) for c in ctx) * 4
+    return {"kv": kv, "q_out": qo, "table": table, "total": kv + qo + table}
+
+
+def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+    """The float64 oracle as it stands, single-threaded, on (sequence, head)
+    pairs in order until the time budget is spent."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                                    # pragma: no cover
+        threadpool_limits = None
+    import oracle.paged as P
+
+    pairs = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_heads)]
+    done, tokens = 0, 0
+    ctx_mgr = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx_mgr:
+        ctx_mgr.__enter__()
+    try:
+        t0 = time.perf_counter()
+        for s, h in pairs:
+            P.paged_decode(wl.q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens,
+                           wl.block_size, wl.scale, wl.dtype, wl.num_kv_heads, pairs=[(s, h)])
+            done += 1
+            tokens += int(wl.context_lens[s])
+            if time.perf_counter() - t0 > budget_s:
+                break
+        el = time.perf_counter() - t0
+    finally:
+        if ctx_mgr:
+            ctx_mgr.__exit__(None, None, None)
+    # one context token of the metric covers all H query heads
+    rate = tokens / wl.num_heads / el
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": rate, "unit": "context tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (sequence, head) pairs of the same workload, "
+                      f"{tokens} head-tokens in {el:.1f} s, float64 numpy, 1 thread on {cpu}"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (default: LLaMA-7B shape)")
+    ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (for counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_cache_368_amd as pa
+    from workloads import make_workload, to_device, to_torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pa.load_library()
+    dev_name = torch.cuda.get_device_name(0)
+    print(f"[bench] device {dev_name}; building workload {args.config}", file=sys.stderr, flush=True)
+    wl = make_workload(args.config, seed=args.seed, block_size=args.block_size)
+    if args.partition_size is not None:
+        wl.partition_size = args.partition_size
+    S, H, Hkv, D, B = wl.num_seqs, wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    dt = wl.dtype
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    maxctx = wl.max_context_len
+    P_used = pa.pa_decode_partition_size(S, H, Hkv, D, B, maxctx, wl.partition_size, tdt)
+    ws_bytes = pa.pa_decode_workspace_size(S, H, Hkv, D, B, maxctx, wl.partition_size, tdt)
+    nbytes = algorithmic_bytes(wl.context_lens, H, Hkv, D, B, dt)
+    sum_ctx = int(wl.context_lens.sum())
+
+    base = to_device(wl)
+    pool_bytes = base.key_cache.numel() * base.key_cache.element_size() * 2
+    copies = max(2, math.ceil(2 * MALL_BYTES / pool_bytes) + 1)
+    pools = [(base.key_cache, base.value_cache)] + [
+        (base.key_cache.clone(), base.value_cache.clone()) for _ in range(copies - 1)]
+    slots = torch.empty(S, dtype=torch.int64, device="cuda")
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: S={S} H={H}/{Hkv} D={D} B={B} {dt} sum(ctx)={sum_ctx} "
+          f"P={P_used} pool copies={copies} ({pool_bytes / 2**20:.0f} MiB each)",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kc, vc = pools[i % copies]
+        pa.pa_compute_slots(slots, base.block_tables, B, wl.num_blocks, context_lens=base.context_lens)
+        pa.pa_cache_write(base.new_key, base.new_value, kc, vc, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_decode(base.out, base.q, kc, vc, base.block_tables, base.context_lens, maxctx,
+                     wl.scale, wl.partition_size, workspace)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
+    dec_mean_s = sum(dec_ms) / len(dec_ms) / 1e3
+    dec_med_s = dec_ms[len(dec_ms) // 2] / 1e3
+    print(f"[bench] {args.steps} steps in {wall * 1e3:.2f} ms; decode mean {dec_mean_s * 1e6:.1f} us "
+          f"median {dec_med_s * 1e6:.1f} us p10 {dec_ms[len(dec_ms) // 10] * 1e3:.1f} us "
+          f"p90 {dec_ms[(9 * len(dec_ms)) // 10] * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    achieved = nbytes["total"] / dec_mean_s / 1e9
+    result = {
+        "metric": METRIC,
+        "value": sum_ctx * args.steps / wall,
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded N(0,1) K/V/q, random block tables; no dataset)",
+        "config": {"workload": wl.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": B, "sum_context_tokens": sum_ctx,
+                   "max_context_len": maxctx, "partition_size": P_used, "seed": wl.seed,
+                   "pool_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "pa_decode (decode kernel + merge pass when split)",
+                     "bytes_per_launch": nbytes["total"], "mean_launch_us": dec_mean_s * 1e6,
+                     "median_launch_us": dec_med_s * 1e6},
+        "decode_context_tokens_per_s": sum_ctx / dec_mean_s,
+        "device": dev_name,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the float64 oracle on a host sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,181 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged KV-cache decode for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources cited below by short key:
+ *   P1  "大模型部署中的PagedAttention：KV Cache显存管理突破" (PagedAttention in LLM
+ *       deployment: a breakthrough in KV-cache memory management),
+ *       blog.csdn.net/qq_22409661/article/details/146144360
+ *   P2  "大模型推理优化：KV Cache与PagedAttention技术详解" (LLM inference
+ *       optimisation: KV cache and PagedAttention explained),
+ *       intelliparadigm.com/article/weixin_32678995/2221576
+ *   P3  "LLM 推理中的 PageAttention 实现原理：虚拟内存管理在 KV Cache 中的创新应用"
+ *       (How PageAttention works in LLM inference), www.dpshk.com/news/3461484/
+ *
+ * Conventions shared by every entry point
+ *   - Every array pointer is a DEVICE pointer to memory the caller owns; the
+ *     library never allocates, frees or keeps device memory, never
+ *     synchronises the host, and launches only on the caller's `stream`
+ *     (NULL = the null stream).  Calls return as soon as the work is queued.
+ *   - Arrays are dense, row-major, with the shapes given per argument.
+ *   - Storage types: PA_F32 (IEEE binary32), PA_F16 (IEEE binary16),
+ *     PA_BF16 (bfloat16).  Arithmetic is float32 throughout.
+ *   - KV pool layout: key_cache and value_cache are each
+ *     [num_blocks][num_kv_heads][block_size][head_dim]: one physical block
+ *     holds block_size consecutive tokens of a sequence (P1 §1, P3 §1), one
+ *     (block, kv head) tile is block_size * head_dim contiguous elements.
+ *   - Token t of sequence s lives in physical block
+ *     block_tables[s][t / block_size] at offset t % block_size (P3 §3, the
+ *     block table's lookup of a token index).  Indices are 0-based.
+ *   - Query head h reads kv head h / (num_heads / num_kv_heads).
+ *   - Errors: a non-OK status means nothing was launched; pa_last_error()
+ *     then describes the failure.  Values that live in device memory
+ *     (context_lens, block ids, slots, positions) cannot be checked by the
+ *     host; the kernels check them instead, as stated per entry point, and
+ *     never read or write outside the arrays described here.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, H % Hkv != 0, ... */
+  PA_ERR_UNSUPPORTED = 2,        /* valid but not built: head_dim, block_size, dtype */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,
+  PA_ERR_HIP = 4                 /* the HIP runtime refused the launch */
+} pa_status_t;
+
+/*
+ * pa_compute_slots -- resolve tokens to pool slots (P3 §3: logical block =
+ * t / B, offset = t % B, physical block = table[logical]; P3 §2: the block
+ * table maps each token to its block).
+ *
+ *   slot_mapping   out  int64 [num_tokens]; slot = phys * block_size + offset,
+ *                       or -1 for a token that has no valid slot.
+ *   block_tables   in   int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens   in   int32 [num_seqs] or NULL (needed when positions is NULL)
+ *   seq_ids        in   int32 [num_tokens] or NULL: token i belongs to
+ *                       sequence seq_ids[i] (NULL: to sequence i)
+ *   positions      in   int32 [num_tokens] or NULL: the token's 0-based
+ *                       position; NULL = the newest token of its sequence,
+ *                       context_lens[seq] - 1 (P2 §2.1: the new token's K/V
+ *                       are appended before attention reads the cache).
+ *
+ * A token gets -1 when its sequence id is outside [0, num_seqs), its position
+ * is negative, its logical block is >= max_blocks_per_seq, or its table entry
+ * is outside [0, num_blocks).
+ */
+pa_status_t pa_compute_slots(int64_t *slot_mapping, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *context_lens,
+                             const int32_t *seq_ids, const int32_t *positions,
+                             int32_t num_tokens, int32_t num_seqs, int32_t block_size,
+                             int32_t num_blocks, hipStream_t stream);
+
+/*
+ * pa_cache_write -- write new tokens' K and V into their pool slots (P2 §2.1
+ * step 3, the current token's K/V join the cache; the slot is the one P3 §3
+ * assigns).  A bit-exact copy:
+ *   key_cache[slot / B][h][slot % B][:] = key[i][h][:]   (same for value)
+ *
+ *   key, value           in     [num_tokens][num_kv_heads][head_dim]
+ *   key_cache, value_cache in/out [num_blocks][num_kv_heads][block_size][head_dim]
+ *   slot_mapping         in     int64 [num_tokens]
+ *
+ * Tokens whose slot is outside [0, num_blocks * block_size) (e.g. -1 padding)
+ * are skipped.  Two tokens with the same slot in one call race: the result
+ * is one of the two rows, unspecified which.
+ * Supported: head_dim % (16 / element bytes) == 0, any block_size >= 1.
+ */
+pa_status_t pa_cache_write(const void *key, const void *value, void *key_cache,
+                           void *value_cache, const int64_t *slot_mapping,
+                           int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, pa_dtype_t dtype,
+                           hipStream_t stream);
+
+/*
+ * pa_decode_partition_size -- the split-context partition length pa_decode
+ * uses for these sizes.  `partition_size` > 0 is validated and returned as
+ * is; 0 asks the library to choose.  Returns -1 for invalid sizes (see
+ * pa_last_error).  A return value >= max_context_len means one partition per
+ * sequence (no merge pass, no workspace).
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_context_len, int32_t partition_size,
+                                 pa_dtype_t dtype);
+
+/*
+ * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for
+ * these sizes (0 when one partition covers max_context_len).  Returns
+ * (size_t)-1 for invalid sizes.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size,
+                                int32_t max_context_len, int32_t partition_size,
+                                pa_dtype_t dtype);
+
+/*
+ * pa_decode -- PagedAttention decode (P1 §1 first formula; P2 §2.1 steps
+ * 4-5; P3 §2, attention gathers each token's K/V through
+ * block_tables[sequence]):
+ *
+ *   out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s
+ *
+ * over tokens t < context_lens[s] of sequence s, K_s/V_s gathered from the
+ * pools through the sequence's block table.  Long contexts are split into
+ * partitions of `partition_size` tokens whose (max, sum, unnormalised
+ * output) states are merged exactly by a log-sum-exp pass.  (P1 §1's second
+ * formula, a sum of per-block softmaxes, is not this quantity and is not
+ * computed.)
+ *
+ *   out            out  [num_seqs][num_heads][head_dim], storage type dtype
+ *   q              in   [num_seqs][num_heads][head_dim]
+ *   key_cache, value_cache in [num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_tables   in   int32 [num_seqs][max_blocks_per_seq]; entries past a
+ *                       sequence's ceil(ctx / block_size) blocks are never read
+ *   context_lens   in   int32 [num_seqs], tokens to attend (the newest
+ *                       token included)
+ *   max_context_len     host-side upper bound on context_lens
+ *   scale               score scale, normally 1/sqrt(head_dim) (P1 §1)
+ *   partition_size      tokens per split-context partition, 0 = choose;
+ *                       must be a multiple of block_size and of 16
+ *   workspace           device memory of >= pa_decode_workspace_size(...)
+ *                       bytes, or NULL when that size is 0
+ *
+ * A sequence with context_lens[s] == 0 gets zeros.  A sequence whose
+ * context_lens value is negative or above max_context_len or
+ * max_blocks_per_seq * block_size, or whose used table entries fall outside
+ * [0, num_blocks), gets NaN in every output element instead of a result.
+ * Supported: head_dim in {64, 128}; block_size in {16, 32, 64};
+ * num_heads % num_kv_heads == 0.
+ */
+pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      pa_dtype_t dtype, hipStream_t stream);
+
+/* Text of the last non-OK status returned on the calling thread. */
+const char *pa_last_error(void);
+
+/* Library version string. */
+const char *pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -133,21 +133,21 @@ def cache_write(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
 # Gather and attention
 # ---------------------------------------------------------------------------
 
-def gather_context(cache64: np.ndarray, table_row, n: int, kv_head: int,
+def gather_context(cache: np.ndarray, table_row, n: int, kv_head: int,
                    block_size: int) -> np.ndarray:
-    """Rows of tokens 0..n-1 of one kv head as a contiguous ``[n][D]`` array:
-    look each token up through the table (P3 §2, §3) and concatenate, as the
-    block-joining helper of P1 §7 does."""
-    D = cache64.shape[-1]
-    out = np.empty((n, D), dtype=np.float64)
+    """Rows of tokens 0..n-1 of one kv head as a contiguous ``[n][D]`` array
+    (same element type as ``cache``): look each token up through the table
+    (P3 §2, §3) and concatenate, as the block-joining helper of P1 §7 does."""
+    D = cache.shape[-1]
+    out = np.empty((n, D), dtype=cache.dtype)
     for t in range(n):
         loc = physical_location(table_row, t, block_size)
         if loc is None:
             raise ValueError(f"token {t} has no block in the table")
         phys, off = loc
-        if not (0 <= phys < cache64.shape[0]):
+        if not (0 <= phys < cache.shape[0]):
             raise ValueError(f"block id {phys} outside the pool")
-        out[t] = cache64[phys, kv_head, off]
+        out[t] = cache[phys, kv_head, off]
     return out
 
 
@@ -168,11 +168,15 @@ def kv_head_of(h: int, num_heads: int, num_kv_heads: int) -> int:
     return h // (num_heads // num_kv_heads)
 
 
-def decode_one(q_row64: np.ndarray, k64: np.ndarray, v64: np.ndarray, table_row, n: int,
-               kv_head: int, block_size: int, scale: float) -> np.ndarray:
-    """Decode output of one (sequence, head): gather, then attend."""
-    K = gather_context(k64, table_row, n, kv_head, block_size)
-    V = gather_context(v64, table_row, n, kv_head, block_size)
+def decode_one(q_row64: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray, table_row,
+               n: int, kv_head: int, block_size: int, scale: float,
+               dtype: str | None = None) -> np.ndarray:
+    """Decode output of one (sequence, head): gather, widen to float64 (when
+    ``dtype`` names the pools' storage type), then attend."""
+    K = gather_context(key_cache, table_row, n, kv_head, block_size)
+    V = gather_context(value_cache, table_row, n, kv_head, block_size)
+    if dtype is not None:
+        K, V = to_f64(K, dtype), to_f64(V, dtype)
     return attention(q_row64, K, V, scale)
 
 
@@ -182,18 +186,16 @@ def paged_decode(q, key_cache, value_cache, block_tables, context_lens, block_si
     """Float64 decode output ``[S][H][D]`` (or only the listed (s, h) pairs,
     others left NaN)."""
     q64 = to_f64(q, dtype)
-    k64 = to_f64(key_cache, dtype)
-    v64 = to_f64(value_cache, dtype)
     S, H, D = q64.shape
-    Hkv = k64.shape[1] if num_kv_heads is None else num_kv_heads
+    Hkv = key_cache.shape[1] if num_kv_heads is None else num_kv_heads
     if H % Hkv:
         raise ValueError("num_heads must be a multiple of num_kv_heads")
     out = np.full((S, H, D), np.nan)
     todo = pairs if pairs is not None else [(s, h) for s in range(S) for h in range(H)]
     for s, h in todo:
         n = int(context_lens[s])
-        out[s, h] = decode_one(q64[s, h], k64, v64, block_tables[s], n,
-                               kv_head_of(h, H, Hkv), block_size, scale)
+        out[s, h] = decode_one(q64[s, h], key_cache, value_cache, block_tables[s], n,
+                               kv_head_of(h, H, Hkv), block_size, scale, dtype)
     return out
 
 

@@ -1,0 +1,20 @@
+"""Paged KV-cache decode for AMD Instinct MI355X (gfx950).
+
+The compute lives in libpa.so (hand-written HIP kernels behind the C ABI of
+include/pa.h); this package is its thin Python binding, plus helpers that move
+the seeded synthetic workloads onto the GPU.
+"""
+from ._capi import (  # noqa: F401
+    DTYPE_CODES,
+    LIB_PATH,
+    PaError,
+    declared_functions,
+    load_library,
+    pa_cache_write,
+    pa_compute_slots,
+    pa_decode,
+    pa_decode_partition_size,
+    pa_decode_workspace_size,
+    pa_last_error,
+    pa_version,
+)

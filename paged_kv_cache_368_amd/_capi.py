@@ -1,0 +1,201 @@
+"""ctypes binding of libpa.so (include/pa.h), same entry-point names.
+
+Argument marshalling only: shapes are read off the tensors, pointers and the
+current HIP stream are passed through, and a non-OK status raises
+``PaError``.  Every computation happens in the library's kernels; there is no
+fallback.  PyTorch is imported first so that the HIP runtime it ships is the
+one libpa.so binds to (both carry the soname libamdhip64.so.7).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
+
+PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP = range(5)
+DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_lib = None
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pa status {status}: {message}")
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Open libpa.so (built by ``paged_kv_cache_368_amd.build``); raises if absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            f"{p} is missing: build it with `python -m paged_kv_cache_368_amd.build`")
+    lib = ctypes.CDLL(p, mode=ctypes.RTLD_GLOBAL)
+    c = ctypes
+    st, i32, ptr, sz = c.c_int, c.c_int32, c.c_void_p, c.c_size_t
+    lib.pa_compute_slots.argtypes = [ptr, ptr, i32, ptr, ptr, ptr, i32, i32, i32, i32, ptr]
+    lib.pa_compute_slots.restype = st
+    lib.pa_cache_write.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, c.c_int, ptr]
+    lib.pa_cache_write.restype = st
+    lib.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, c.c_int]
+    lib.pa_decode_partition_size.restype = i32
+    lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, c.c_int]
+    lib.pa_decode_workspace_size.restype = sz
+    lib.pa_decode.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, i32, i32, i32,
+                              c.c_float, i32, ptr, sz, c.c_int, ptr]
+    lib.pa_decode.restype = st
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = c.c_char_p
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = c.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def declared_functions(header: str = HEADER) -> list[str]:
+    """Names of the functions include/pa.h declares."""
+    with open(header) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        raise PaError(status, load_library().pa_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _opt(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def pa_version() -> str:
+    return load_library().pa_version().decode()
+
+
+def pa_last_error() -> str:
+    return load_library().pa_last_error().decode()
+
+
+def pa_compute_slots(slot_mapping: torch.Tensor, block_tables: torch.Tensor, block_size: int,
+                     num_blocks: int, context_lens: torch.Tensor | None = None,
+                     seq_ids: torch.Tensor | None = None,
+                     positions: torch.Tensor | None = None) -> torch.Tensor:
+    """Fill int64 ``slot_mapping`` with the pool slot of each token."""
+    lib = load_library()
+    for n, t in (("slot_mapping", slot_mapping), ("block_tables", block_tables)):
+        _dev(t, n)
+    if slot_mapping.dtype != torch.int64 or block_tables.dtype != torch.int32:
+        raise ValueError("slot_mapping must be int64 and block_tables int32")
+    for n, t in (("context_lens", context_lens), ("seq_ids", seq_ids), ("positions", positions)):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != torch.int32:
+                raise ValueError(f"{n} must be int32")
+    _check(lib.pa_compute_slots(
+        ctypes.c_void_p(slot_mapping.data_ptr()), ctypes.c_void_p(block_tables.data_ptr()),
+        block_tables.shape[1], _opt(context_lens), _opt(seq_ids), _opt(positions),
+        slot_mapping.numel(), block_tables.shape[0], block_size, num_blocks, _stream(slot_mapping)))
+    return slot_mapping
+
+
+def pa_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                   value_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Copy key/value [T][Hkv][D] into the pools [NB][Hkv][B][D] at their slots."""
+    lib = load_library()
+    for n, t in (("key", key), ("value", value), ("key_cache", key_cache),
+                 ("value_cache", value_cache), ("slot_mapping", slot_mapping)):
+        _dev(t, n)
+    if key.dtype not in DTYPE_CODES or any(t.dtype != key.dtype for t in (value, key_cache, value_cache)):
+        raise ValueError("key, value and the pools must share one of float32/float16/bfloat16")
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    NB, Hkv, B, D = key_cache.shape
+    if tuple(value_cache.shape) != (NB, Hkv, B, D) or key.shape[1:] != (Hkv, D) or value.shape != key.shape:
+        raise ValueError("shape mismatch between key/value and the pools")
+    if slot_mapping.numel() != key.shape[0]:
+        raise ValueError("slot_mapping must have one entry per token")
+    _check(lib.pa_cache_write(
+        ctypes.c_void_p(key.data_ptr()), ctypes.c_void_p(value.data_ptr()),
+        ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
+        ctypes.c_void_p(slot_mapping.data_ptr()), key.shape[0], Hkv, D, B, NB,
+        DTYPE_CODES[key.dtype], _stream(key)))
+
+
+def pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                             max_context_len, partition_size=0, dtype=torch.float16) -> int:
+    return load_library().pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                   block_size, max_context_len, partition_size,
+                                                   DTYPE_CODES[dtype])
+
+
+def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                             max_context_len, partition_size=0, dtype=torch.float16) -> int:
+    n = load_library().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                block_size, max_context_len, partition_size,
+                                                DTYPE_CODES[dtype])
+    if n == ctypes.c_size_t(-1).value:
+        raise PaError(PA_ERR_INVALID_ARGUMENT, pa_last_error())
+    return n
+
+
+def pa_decode(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+              value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+              max_context_len: int, scale: float | None = None, partition_size: int = 0,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """PagedAttention decode into ``out`` [S][H][D]; see include/pa.h.
+
+    ``workspace`` (uint8, >= pa_decode_workspace_size bytes) may be passed to
+    keep the call free of allocation; otherwise one is allocated here.
+    """
+    lib = load_library()
+    for n, t in (("out", out), ("q", q), ("key_cache", key_cache), ("value_cache", value_cache),
+                 ("block_tables", block_tables), ("context_lens", context_lens)):
+        _dev(t, n)
+    if q.dtype not in DTYPE_CODES or any(t.dtype != q.dtype for t in (out, key_cache, value_cache)):
+        raise ValueError("q, out and the pools must share one of float32/float16/bfloat16")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    S, H, D = q.shape
+    NB, Hkv, B, D2 = key_cache.shape
+    if D2 != D or tuple(value_cache.shape) != (NB, Hkv, B, D) or tuple(out.shape) != (S, H, D):
+        raise ValueError("shape mismatch between q, out and the pools")
+    if block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables and context_lens must have one row per sequence")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dt = DTYPE_CODES[q.dtype]
+    need = pa_decode_workspace_size(S, H, Hkv, D, B, max_context_len, partition_size, q.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode(
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(context_lens.data_ptr()),
+        S, H, Hkv, D, B, NB, block_tables.shape[1], max_context_len, float(scale),
+        partition_size, ws_ptr, ws_bytes, dt, _stream(q)))
+    return out

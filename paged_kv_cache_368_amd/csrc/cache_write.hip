@@ -1,0 +1,92 @@
+// Paged cache write (reshape-and-cache) and slot resolution for gfx950.
+//
+// cache write: each new token's K and V rows are copied bit for bit into
+// their pool slot (P2 §2.1 step 3: the current token's K/V join the cache),
+//   key_cache[slot / B][h][slot % B][:] = key[i][h][:].
+// One thread moves one 16-byte piece of a K row and the matching piece of the
+// V row; a wave covers whole contiguous rows, so loads and stores are full
+// 16-byte accesses.
+//
+// slot resolution (P3 §3): logical block = t / B, offset = t % B,
+// slot = block_tables[seq][logical] * B + offset.
+#include "pa_device.h"
+
+namespace pa {
+
+namespace {
+
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    const u32x4 *__restrict__ key, const u32x4 *__restrict__ value, u32x4 *__restrict__ key_cache,
+    u32x4 *__restrict__ value_cache, const int64_t *__restrict__ slot_mapping, int num_tokens,
+    int num_kv_heads, int row_units, int block_size, long long pool_slots) {
+  const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long per_token = (long long)num_kv_heads * row_units;
+  if (u >= per_token * num_tokens) return;
+  const int i = (int)(u / per_token);
+  const int rem = (int)(u - (long long)i * per_token);     // h * row_units + c
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= pool_slots) return;
+  const long long blk = slot / block_size;
+  const int off = (int)(slot - blk * block_size);
+  const int h = rem / row_units;
+  const int c = rem - h * row_units;
+  const long long dst = ((blk * num_kv_heads + h) * block_size + off) * row_units + c;
+  key_cache[dst] = key[u];
+  value_cache[dst] = value[u];
+}
+
+__global__ __launch_bounds__(256) void compute_slots_kernel(
+    int64_t *__restrict__ slot_mapping, const int32_t *__restrict__ block_tables,
+    int max_blocks_per_seq, const int32_t *__restrict__ context_lens,
+    const int32_t *__restrict__ seq_ids, const int32_t *__restrict__ positions, int num_tokens,
+    int num_seqs, int block_size, int num_blocks) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= num_tokens) return;
+  int64_t slot = -1;
+  const int s = seq_ids ? seq_ids[i] : i;
+  if (s >= 0 && s < num_seqs) {
+    const int pos = positions ? positions[i] : context_lens[s] - 1;
+    if (pos >= 0) {
+      const int logical = pos / block_size;
+      const int offset = pos - logical * block_size;
+      if (logical < max_blocks_per_seq) {
+        const int phys = block_tables[(size_t)s * max_blocks_per_seq + logical];
+        if (phys >= 0 && phys < num_blocks) slot = (int64_t)phys * block_size + offset;
+      }
+    }
+  }
+  slot_mapping[i] = slot;
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const void *key, const void *value, void *key_cache,
+                              void *value_cache, const int64_t *slot_mapping, int num_tokens,
+                              int num_kv_heads, int row_bytes, int block_size, int num_blocks,
+                              hipStream_t stream) {
+  const int row_units = row_bytes / 16;
+  const long long total = (long long)num_tokens * num_kv_heads * row_units;
+  if (total <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL(cache_write_kernel, dim3(grid), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4 *>(key), reinterpret_cast<const u32x4 *>(value),
+                     reinterpret_cast<u32x4 *>(key_cache), reinterpret_cast<u32x4 *>(value_cache),
+                     slot_mapping, num_tokens, num_kv_heads, row_units, block_size,
+                     (long long)num_blocks * block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_compute_slots(int64_t *slot_mapping, const int32_t *block_tables,
+                                int max_blocks_per_seq, const int32_t *context_lens,
+                                const int32_t *seq_ids, const int32_t *positions,
+                                int num_tokens, int num_seqs, int block_size, int num_blocks,
+                                hipStream_t stream) {
+  if (num_tokens <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((num_tokens + 255) / 256);
+  hipLaunchKernelGGL(compute_slots_kernel, dim3(grid), dim3(256), 0, stream, slot_mapping,
+                     block_tables, max_blocks_per_seq, context_lens, seq_ids, positions,
+                     num_tokens, num_seqs, block_size, num_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,405 @@
+// PagedAttention decode on the vector ALUs, and the log-sum-exp merge of
+// split-context partitions, for gfx950.
+//
+// What is computed (P1 §1, first formula; P2 §2.1 steps 4-5; P3 §2): for
+// sequence s and query head h,
+//     out[s][h] = softmax(scale * q[s][h] . K^T) V
+// over the s's first context_lens[s] tokens, each token's K/V row fetched
+// from the physical block block_tables[s][t / B] at offset t % B (P3 §3).
+//
+// Work decomposition.  One work-group of 4 waves owns one (sequence, head,
+// partition).  The partition's slice of the block table is staged once into
+// LDS; each wave then keeps the ids of the chunks it owns in one VGPR (lane k
+// = its k-th chunk) and reads them with v_readlane, so no dependent memory
+// load sits between one chunk's K/V loads and the next.  Waves take the
+// partition's 16-token chunks round-robin, so at any moment the work-group
+// streams four neighbouring chunks.
+//
+// Lane layout.  A K or V row of one token is D * elem bytes = LPT lanes x 16
+// bytes (LPT = 16 for fp16/bf16 D=128 and fp32 D=64), so one 16-byte load per
+// lane covers 64/LPT whole rows and every load of the wave is one contiguous
+// kilobyte.  A lane's partial q.k is reduced over its LPT-lane row with DPP;
+// each row keeps its own online-softmax state (running max m, running sum l,
+// unnormalised output o) for the tokens that land on it, so the inner loop
+// has no cross-row traffic at all.  Rows, then waves, are merged once at the
+// end with the same max-rescaled sums.
+//
+// Pipelining.  K and V of chunk k+1 are issued before chunk k is consumed
+// (double-buffered registers), the in-kernel form of P1 §4's "load the next
+// block while computing the current one".
+//
+// Masking.  Tokens past the context in the last chunk get score -inf and
+// their V words are zeroed by select, so whatever the unused slots hold
+// (NaN in the tests) never reaches the result.
+#include "pa_device.h"
+
+namespace pa {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+
+template <int DT, int D>
+struct MhaShape {
+  static constexpr int kE = Storage<DT>::kBytes;
+  static constexpr int kEpl = 16 / kE;          // elements per lane per load
+  static constexpr int kLpt = D / kEpl;         // lanes per token row
+  static constexpr int kTpl = 64 / kLpt;        // token rows per wave load
+  static constexpr int kLoads = kChunk / kTpl;  // loads per chunk, K and V each
+  static_assert(kLpt == 8 || kLpt == 16 || kLpt == 32, "row width");
+};
+
+// Per-lane dot of the lane's 16 bytes of q and of a K row.
+template <int DT>
+__device__ __forceinline__ float lane_dot(const u32x4 &q, const u32x4 &k) {
+  if constexpr (DT == kF32) {
+    float acc = as_f32(q.x) * as_f32(k.x);
+    acc = __builtin_fmaf(as_f32(q.y), as_f32(k.y), acc);
+    acc = __builtin_fmaf(as_f32(q.z), as_f32(k.z), acc);
+    acc = __builtin_fmaf(as_f32(q.w), as_f32(k.w), acc);
+    return acc;
+  } else {
+    float acc = dot2<DT>(q.x, k.x, 0.f);
+    acc = dot2<DT>(q.y, k.y, acc);
+    acc = dot2<DT>(q.z, k.z, acc);
+    acc = dot2<DT>(q.w, k.w, acc);
+    return acc;
+  }
+}
+
+// o[0..EPL) += p * (the lane's 16 bytes of a V row)
+template <int DT>
+__device__ __forceinline__ void lane_axpy(float *o, float p, const u32x4 &v) {
+  if constexpr (DT == kF32) {
+    o[0] = __builtin_fmaf(p, as_f32(v.x), o[0]);
+    o[1] = __builtin_fmaf(p, as_f32(v.y), o[1]);
+    o[2] = __builtin_fmaf(p, as_f32(v.z), o[2]);
+    o[3] = __builtin_fmaf(p, as_f32(v.w), o[3]);
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __builtin_fmaf(p, lo_f32<DT>(w[i]), o[2 * i]);
+      o[2 * i + 1] = __builtin_fmaf(p, hi_f32<DT>(w[i]), o[2 * i + 1]);
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_out(void *base, size_t elem, const float *o, int n) {
+  if constexpr (DT == kF32) {
+    float *p = reinterpret_cast<float *>(base) + elem;
+    for (int i = 0; i < n; ++i) p[i] = o[i];
+  } else {
+    uint16_t *p = reinterpret_cast<uint16_t *>(base) + elem;
+    for (int i = 0; i < n; ++i)
+      p[i] = (uint16_t)(DT == kF16 ? f32_to_f16_bits(o[i]) : f32_to_bf16_bits(o[i]));
+  }
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
+  using Sh = MhaShape<DT, D>;
+  constexpr int E = Sh::kE, EPL = Sh::kEpl, LPT = Sh::kLpt, TPL = Sh::kTpl, NL = Sh::kLoads;
+
+  __shared__ int s_tbl[kMaxPartBlocks];
+  __shared__ float s_o[kWaves][D];
+  __shared__ float s_m[kWaves], s_l[kWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+
+  const int H = a.num_heads, S = a.num_seqs;
+  const int item = xcd_logical_index(blockIdx.x, gridDim.x);
+  const int h = item % H;
+  const int s = (item / H) % S;
+  const int p = item / (H * S);
+
+  const int P = a.partition_size;
+  const int ctx = a.context_lens[s];
+  const bool bad_ctx = ctx < 0 || ctx > a.max_context_len ||
+                       ctx > a.max_blocks_per_seq * a.block_size;
+  const int nps = bad_ctx ? 1 : (ctx + P - 1) / P;
+  if (p >= (nps > 0 ? nps : 1)) return;           // uniform over the work-group
+  const bool direct = nps <= 1;
+
+  const int t0 = p * P;
+  const int t1 = bad_ctx ? t0 : min(t0 + P, ctx);
+  const int b0 = t0 >> a.log2_block;
+  const int nblk = bad_ctx ? 0 : ((t1 - t0 + a.block_size - 1) >> a.log2_block);
+
+  // Stage the partition's block ids; flag any id outside the pool.
+  bool bad_id = false;
+  const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks_per_seq + b0;
+  for (int i = tid; i < nblk; i += 256) {
+    const int id = trow[i];
+    bad_id |= (id < 0) | (id >= a.num_blocks);
+    s_tbl[i] = id;
+  }
+  const bool poison = __syncthreads_or(bad_id) || bad_ctx;
+
+  const size_t row_out = ((size_t)s * H + h) * D;
+  const size_t part = ((size_t)s * H + h) * a.num_partitions + p;
+  if (poison) {
+    const float nan = __builtin_nanf("");
+    if (direct) {
+      if (tid < D) {
+        float v = nan;
+        store_out<DT>(a.out, row_out + tid, &v, 1);
+      }
+    } else {
+      if (tid < D) a.ws_o[part * D + tid] = nan;
+      if (tid == 0) {
+        a.ws_ml[2 * part] = __builtin_inff();
+        a.ws_ml[2 * part + 1] = nan;
+      }
+    }
+    return;
+  }
+
+  const int G = H / a.num_kv_heads;
+  const int kvh = h / G;
+  const int row = lane / LPT;
+  const int col = lane % LPT;
+
+  // q: every row of the wave holds the same 16-byte slice of q[s][h].
+  const u32x4 qv = *reinterpret_cast<const u32x4 *>(
+      reinterpret_cast<const char *>(a.q) + (row_out + col * EPL) * E);
+
+  const int nch = (t1 - t0 + kChunk - 1) / kChunk;
+  const int nch_w = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;
+  // This wave's chunk k is partition chunk wave + 4k; lane k keeps its block id.
+  int my_ids = 0;
+  if (lane < nch_w) my_ids = s_tbl[((wave + kWaves * lane) * kChunk) >> a.log2_block];
+
+  const size_t head_stride = (size_t)a.block_size * D;        // elements per (block, head) tile
+  const size_t block_stride = head_stride * a.num_kv_heads;
+  const char *kbase = reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E;
+  const char *vbase = reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E;
+  const int lane_off = (row * D + col * EPL) * E;
+
+  // Byte offset (from the kv head's first tile) of this wave's chunk k.
+  auto chunk_offset = [&](int k) -> size_t {
+    const int phys = __builtin_amdgcn_readlane(my_ids, k);
+    const int tok = (wave + kWaves * k) * kChunk;             // relative to t0, block aligned
+    const int off = tok & (a.block_size - 1);
+    return ((size_t)phys * block_stride + (size_t)off * D) * E;
+  };
+
+  // K and V of one chunk are read through two buffer descriptors whose base
+  // is the chunk's first row (scalar registers) and whose range is the chunk:
+  // every lane then needs only its 32-bit offset, and nothing outside the
+  // chunk can be touched.
+  constexpr int kChunkBytes = kChunk * D * E;
+  auto load = [&](u32x4 *kb, u32x4 *vb, int k) {
+    const size_t off = chunk_offset(k);
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, kChunkBytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, kChunkBytes, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+      kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + j * TPL * D * E, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+      vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + j * TPL * D * E, 0, 0);
+    // Keep the scheduler from sinking these loads below the compute that
+    // follows: they must be in flight while the previous chunk is consumed.
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  float m = kNegInf, l = 0.f;
+  float o[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) o[i] = 0.f;
+
+  auto consume = [&](const u32x4 *kb, const u32x4 *vb, int k) {
+    const int tc = t0 + (wave + kWaves * k) * kChunk;
+    float sc[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) sc[j] = group_sum<LPT>(lane_dot<DT>(qv, kb[j])) * a.scale_log2;
+    const bool tail = tc + kChunk > t1;                       // last chunk: mask past the context
+    bool valid[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      valid[j] = !tail || (tc + j * TPL + row < t1);
+      sc[j] = valid[j] ? sc[j] : kNegInf;
+    }
+    float mloc = sc[0];
+#pragma unroll
+    for (int j = 1; j < NL; ++j) mloc = fmaxf(mloc, sc[j]);
+    const float mnew = fmaxf(m, mloc);
+    const float msafe = mnew == kNegInf ? 0.f : mnew;
+    const float corr = exp2_fast(m - msafe);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] *= corr;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const float pj = exp2_fast(sc[j] - msafe);
+      psum += pj;
+      const u32x4 v = valid[j] ? vb[j] : u32x4{0u, 0u, 0u, 0u};
+      lane_axpy<DT>(o, pj, v);
+    }
+    l = l * corr + psum;
+    m = mnew;
+  };
+
+  // Two chunks per trip, each buffer reloaded right after it is consumed.
+  // The reload past the last chunk is clamped to it (an L2 hit, not used).
+  u32x4 kb0[NL], vb0[NL], kb1[NL], vb1[NL];
+  if (nch_w > 0) {
+    load(kb0, vb0, 0);
+    int k = 0;
+    for (; k + 1 < nch_w; k += 2) {
+      load(kb1, vb1, k + 1);
+      consume(kb0, vb0, k);
+      load(kb0, vb0, min(k + 2, nch_w - 1));
+      consume(kb1, vb1, k + 1);
+    }
+    if (k < nch_w) consume(kb0, vb0, k);
+  }
+
+  // Merge the rows of this wave (lanes with equal col, different row).
+  float M = m;
+#pragma unroll
+  for (int msk = LPT; msk < 64; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk));
+  {
+    const float Ms = M == kNegInf ? 0.f : M;
+    const float w = exp2_fast(m - Ms);
+    l *= w;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] *= w;
+  }
+#pragma unroll
+  for (int msk = LPT; msk < 64; msk <<= 1) {
+    l += __shfl_xor(l, msk);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] += __shfl_xor(o[i], msk);
+  }
+  if (row == 0) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) s_o[wave][col * EPL + i] = o[i];
+    if (col == 0) {
+      s_m[wave] = M;
+      s_l[wave] = l;
+    }
+  }
+  __syncthreads();
+
+  // Merge the 4 waves; thread d < D owns output element d.
+  if (tid < D) {
+    float Mw = s_m[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) Mw = fmaxf(Mw, s_m[w]);
+    const float Ms = Mw == kNegInf ? 0.f : Mw;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = exp2_fast(s_m[w] - Ms);
+      L += f * s_l[w];
+      O += f * s_o[w][tid];
+    }
+    if (direct) {
+      const float r = L == 0.f ? 0.f : O / L;   // NaN (a poisoned partition) propagates
+      store_out<DT>(a.out, row_out + tid, &r, 1);
+    } else {
+      a.ws_o[part * D + tid] = O;
+      if (tid == 0) {
+        a.ws_ml[2 * part] = Mw;
+        a.ws_ml[2 * part + 1] = L;
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of split-context partitions: one wave per (s, h).
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
+// Sequences that fit one partition were written directly and are skipped.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+  constexpr int PER = D / 64;                  // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int H = a.num_heads;
+  if (item >= a.num_seqs * H) return;
+  const int s = item / H;
+  const int ctx = a.context_lens[s];
+  const int P = a.partition_size;
+  if (ctx < 0 || ctx > a.max_context_len || ctx > a.max_blocks_per_seq * a.block_size) return;
+  const int nps = (ctx + P - 1) / P;
+  if (nps <= 1) return;
+
+  const size_t base = (size_t)item * a.num_partitions;
+  float M = kNegInf;
+  for (int p = lane; p < nps; p += 64) M = fmaxf(M, a.ws_ml[2 * (base + p)]);
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk));
+  const float Ms = M == kNegInf ? 0.f : M;
+
+  float L = 0.f;
+  float O[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) O[i] = 0.f;
+  for (int p0 = 0; p0 < nps; p0 += 64) {
+    const int p = p0 + lane;
+    float f = 0.f;
+    if (p < nps) {
+      f = exp2_fast(a.ws_ml[2 * (base + p)] - Ms);
+      L += f * a.ws_ml[2 * (base + p) + 1];
+    }
+    const int n = min(64, nps - p0);
+    for (int j = 0; j < n; ++j) {
+      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+      const float *src = a.ws_o + (base + p0 + j) * D + lane * PER;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) O[i] = __builtin_fmaf(fj, src[i], O[i]);
+    }
+  }
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) L += __shfl_xor(L, msk);
+  float r[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) r[i] = L == 0.f ? 0.f : O[i] / L;
+  store_out<DT>(a.out, (size_t)item * D + lane * PER, r, PER);
+}
+
+template <int DT, int D>
+hipError_t launch_mha_t(const DecodeArgs &a, hipStream_t stream) {
+  const long n = (long)a.num_seqs * a.num_heads * a.num_partitions;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_mha_kernel<DT, D>), dim3((unsigned)n), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_merge_t(const DecodeArgs &a, hipStream_t stream) {
+  const long n = ((long)a.num_seqs * a.num_heads + kWaves - 1) / kWaves;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3((unsigned)n), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#define PA_DISPATCH(FN, dt, D, ...)                                        \
+  switch (dt * 1000 + D) {                                                 \
+    case kF32 * 1000 + 64: return FN<kF32, 64>(__VA_ARGS__);               \
+    case kF32 * 1000 + 128: return FN<kF32, 128>(__VA_ARGS__);             \
+    case kF16 * 1000 + 64: return FN<kF16, 64>(__VA_ARGS__);               \
+    case kF16 * 1000 + 128: return FN<kF16, 128>(__VA_ARGS__);             \
+    case kBF16 * 1000 + 64: return FN<kBF16, 64>(__VA_ARGS__);             \
+    case kBF16 * 1000 + 128: return FN<kBF16, 128>(__VA_ARGS__);           \
+    default: return hipErrorInvalidValue;                                  \
+  }
+
+hipError_t launch_decode_mha(const DecodeArgs &a, int dt, hipStream_t stream) {
+  PA_DISPATCH(launch_mha_t, dt, a.head_dim, a, stream)
+}
+
+hipError_t launch_merge(const DecodeArgs &a, int dt, hipStream_t stream) {
+  PA_DISPATCH(launch_merge_t, dt, a.head_dim, a, stream)
+}
+
+}  // namespace pa

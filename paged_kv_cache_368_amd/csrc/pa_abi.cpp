@@ -1,0 +1,233 @@
+// C ABI of libpa.so (declared in include/pa.h): argument validation, the
+// choice of split-context partition length, workspace sizing and kernel
+// dispatch.  Allocates nothing, never synchronises, launches on the caller's
+// stream.
+#include "pa.h"
+
+#include <math.h>
+
+#include <string>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status_t fail(pa_status_t st, const std::string &msg) {
+  g_last_error = msg;
+  return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Work-groups the auto choice aims for: enough to keep every CU of the chip
+// busy with several resident work-groups while short partitions stay rare.
+constexpr long long kTargetWorkgroups = 2048;
+
+struct Sizes {
+  int partition;
+  int num_partitions;
+  size_t ws_o_bytes;
+  size_t ws_bytes;
+};
+
+pa_status_t check_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                        pa_dtype_t dtype) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
+  if (num_heads <= 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_heads and num_kv_heads must be > 0");
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_heads must be a multiple of num_kv_heads");
+  if (max_context_len < 0) return fail(PA_ERR_INVALID_ARGUMENT, "max_context_len must be >= 0");
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "dtype must be PA_F32, PA_F16 or PA_BF16");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (block_size != 16 && block_size != 32 && block_size != 64)
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be 16, 32 or 64");
+  return PA_OK;
+}
+
+pa_status_t plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t block_size, int32_t max_context_len, int32_t partition_size,
+                 pa_dtype_t dtype, Sizes *out) {
+  pa_status_t st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                               max_context_len, dtype);
+  if (st != PA_OK) return st;
+  int P = partition_size;
+  if (P < 0) return fail(PA_ERR_INVALID_ARGUMENT, "partition_size must be >= 0");
+  if (P > 0) {
+    if (P % block_size != 0 || P % pa::kChunk != 0)
+      return fail(PA_ERR_INVALID_ARGUMENT,
+                  "partition_size must be a multiple of block_size and of 16");
+    if (P > pa::kMaxPartition)
+      return fail(PA_ERR_UNSUPPORTED, "partition_size above 4096 tokens is not supported");
+  } else {
+    const long long items = (long long)num_seqs * num_heads;
+    P = pa::kMaxPartition;
+    while (P > 256 && items * ceil_div(max_context_len, P) < kTargetWorkgroups) P /= 2;
+  }
+  const long long np = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
+  if ((long long)num_seqs * num_heads * np > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "too many (sequence, head, partition) work items");
+  out->partition = P;
+  out->num_partitions = (int)np;
+  out->ws_o_bytes = 0;
+  out->ws_bytes = 0;
+  if (np > 1) {
+    const size_t parts = (size_t)num_seqs * num_heads * (size_t)np;
+    out->ws_o_bytes = (parts * head_dim * sizeof(float) + 255) & ~(size_t)255;
+    out->ws_bytes = out->ws_o_bytes + parts * 2 * sizeof(float);
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_last_error(void) { return g_last_error.c_str(); }
+
+const char *pa_version(void) { return "pa 0.1.0 gfx950"; }
+
+pa_status_t pa_compute_slots(int64_t *slot_mapping, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *context_lens,
+                             const int32_t *seq_ids, const int32_t *positions,
+                             int32_t num_tokens, int32_t num_seqs, int32_t block_size,
+                             int32_t num_blocks, hipStream_t stream) {
+  if (num_tokens < 0 || num_seqs < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens and num_seqs must be >= 0");
+  if (num_tokens == 0) return PA_OK;
+  if (!slot_mapping || !block_tables)
+    return fail(PA_ERR_INVALID_ARGUMENT, "slot_mapping and block_tables must not be NULL");
+  if (!positions && !context_lens)
+    return fail(PA_ERR_INVALID_ARGUMENT, "positions or context_lens must be given");
+  if (max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "max_blocks_per_seq, block_size and num_blocks must be > 0");
+  hipError_t e = pa::launch_compute_slots(slot_mapping, block_tables, max_blocks_per_seq,
+                                          context_lens, seq_ids, positions, num_tokens,
+                                          num_seqs, block_size, num_blocks, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+pa_status_t pa_cache_write(const void *key, const void *value, void *key_cache,
+                           void *value_cache, const int64_t *slot_mapping,
+                           int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, pa_dtype_t dtype,
+                           hipStream_t stream) {
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "dtype must be PA_F32, PA_F16 or PA_BF16");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0");
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "num_kv_heads, head_dim, block_size and num_blocks must be > 0");
+  const int row_bytes = head_dim * pa::elem_bytes(dtype);
+  if (row_bytes % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim * element bytes must be a multiple of 16");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pointer arguments must not be NULL");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "key, value and the pools must be 16-byte aligned");
+  hipError_t e = pa::launch_cache_write(key, value, key_cache, value_cache, slot_mapping,
+                                        num_tokens, num_kv_heads, row_bytes, block_size,
+                                        num_blocks, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_context_len, int32_t partition_size,
+                                 pa_dtype_t dtype) {
+  Sizes z;
+  if (plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+           partition_size, dtype, &z) != PA_OK)
+    return -1;
+  return z.partition;
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size,
+                                int32_t max_context_len, int32_t partition_size,
+                                pa_dtype_t dtype) {
+  Sizes z;
+  if (plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+           partition_size, dtype, &z) != PA_OK)
+    return (size_t)-1;
+  return z.ws_bytes;
+}
+
+pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      pa_dtype_t dtype, hipStream_t stream) {
+  Sizes z;
+  pa_status_t st = plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_context_len, partition_size, dtype, &z);
+  if (st != PA_OK) return st;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks and max_blocks_per_seq must be > 0");
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "max_context_len exceeds max_blocks_per_seq * block_size");
+  if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pointer arguments must not be NULL");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "out, q and the pools must be 16-byte aligned");
+  if (z.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < z.ws_bytes)
+      return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                  "workspace smaller than pa_decode_workspace_size() = " +
+                      std::to_string(z.ws_bytes) + " bytes");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(PA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  }
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.ws_o = static_cast<float *>(workspace);
+  a.ws_ml = z.ws_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + z.ws_o_bytes)
+                       : nullptr;
+  a.q = q;
+  a.k_cache = key_cache;
+  a.v_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.log2_block = ilog2(block_size);
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.partition_size = z.partition;
+  a.num_partitions = z.num_partitions;
+
+  hipError_t e = pa::launch_decode_mha(a, dtype, stream);
+  if (e == hipSuccess && z.num_partitions > 1) e = pa::launch_merge(a, dtype, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Device-side helpers shared by the gfx950 kernels: storage decoding, 16-byte
+// vector types, DPP row reductions and the XCD-aware work-group order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---- storage words ---------------------------------------------------------
+
+// Reinterpret a 32-bit word as float.  Takes the word by value on purpose:
+// hipcc's __builtin_bit_cast applied directly to an ext_vector element
+// (v.y, v.z, ...) reads element 0 instead, so vector elements must be copied
+// to a scalar first.
+__device__ __forceinline__ float as_f32(uint32_t w) { return __builtin_bit_cast(float, w); }
+
+template <int DT> struct Storage;
+template <> struct Storage<kF32> { static constexpr int kBytes = 4; };
+template <> struct Storage<kF16> { static constexpr int kBytes = 2; };
+template <> struct Storage<kBF16> { static constexpr int kBytes = 2; };
+
+// Widen the two 16-bit values packed in a 32-bit word.
+template <int DT> __device__ __forceinline__ float lo_f32(uint32_t w);
+template <int DT> __device__ __forceinline__ float hi_f32(uint32_t w);
+template <> __device__ __forceinline__ float lo_f32<kF16>(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w).x;
+}
+template <> __device__ __forceinline__ float hi_f32<kF16>(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w).y;
+}
+template <> __device__ __forceinline__ float lo_f32<kBF16>(uint32_t w) {
+  return __builtin_bit_cast(float, w << 16);
+}
+template <> __device__ __forceinline__ float hi_f32<kBF16>(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi on the packed dot units; products of two
+// 16-bit values are exact in float32.
+template <int DT> __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc);
+template <> __device__ __forceinline__ float dot2<kF16>(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc,
+                                false);
+}
+template <> __device__ __forceinline__ float dot2<kBF16>(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+// Round float32 to the storage type, nearest-even; returns the storage bits.
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
+  _Float16 h = (_Float16)x;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t b = __builtin_bit_cast(uint32_t, x);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays a quiet NaN
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+// ---- cross-lane ------------------------------------------------------------
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;     // within a 16-lane row this is lane ^ 8
+constexpr int kDppRowHalfMirror = 0x141;
+
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of N lanes (N in {8, 16, 32}); every lane of the
+// group receives the total.
+template <int N> __device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16 || N == 32, "group");
+  if constexpr (N == 8) {
+    v += dpp<kDppRowHalfMirror>(v);
+  } else {
+    v += dpp<kDppRowRor8>(v);
+    v += dpp<kDppRowRor4>(v);
+  }
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppQuadXor1>(v);
+  if constexpr (N == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+// ---- work-group order --------------------------------------------------------
+
+// Work-groups are handed to the 8 XCDs round-robin by hardware id.  Return a
+// logical index such that consecutive logical indices run on the same XCD
+// (and so share its L2), while the hardware dispatch order is unchanged.
+__device__ __forceinline__ int xcd_logical_index(int hw_id, int n) {
+  constexpr int kXcd = 8;
+  const int per = n / kXcd, extra = n % kXcd;
+  const int x = hw_id % kXcd, k = hw_id / kXcd;
+  return x * per + (x < extra ? x : extra) + k;
+}
+
+// Word 3 of a raw (untyped, unswizzled) buffer descriptor on CDNA3/CDNA4.
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

@@ -1,0 +1,53 @@
+// Internal launch interface between the C ABI (pa_abi.cpp) and the kernels.
+// Not installed; the public surface is include/pa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum Dt : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+inline int elem_bytes(int dt) { return dt == kF32 ? 4 : 2; }
+
+// Longest partition one work-group handles: 256 chunks of 16 tokens.  Bounded
+// by the per-wave block-id register (64 lanes x 4 waves) and by the LDS copy
+// of the partition's table slice.
+constexpr int kMaxPartition = 4096;
+constexpr int kChunk = 16;            // tokens per inner-loop step of a wave
+constexpr int kWaves = 4;             // waves per work-group
+constexpr int kMaxPartBlocks = kMaxPartition / 16;
+
+struct DecodeArgs {
+  void *out;                 // [S][H][D] storage dtype
+  float *ws_o;               // [S][H][NP][D] fp32, unnormalised partial outputs
+  float *ws_ml;              // [S][H][NP][2] fp32, (max score in log2 units, sum)
+  const void *q;             // [S][H][D]
+  const void *k_cache;       // [NB][Hkv][B][D]
+  const void *v_cache;
+  const int32_t *block_tables;  // [S][MB]
+  const int32_t *context_lens;  // [S]
+  int num_seqs, num_heads, num_kv_heads, head_dim;
+  int block_size, log2_block, num_blocks, max_blocks_per_seq, max_context_len;
+  float scale_log2;          // scale * log2(e): scores live in base-2 units
+  int partition_size;        // P
+  int num_partitions;        // NP = ceil(max_context_len / P), >= 1
+};
+
+hipError_t launch_decode_mha(const DecodeArgs &a, int dt, hipStream_t stream);
+hipError_t launch_merge(const DecodeArgs &a, int dt, hipStream_t stream);
+
+hipError_t launch_cache_write(const void *key, const void *value, void *key_cache,
+                              void *value_cache, const int64_t *slot_mapping, int num_tokens,
+                              int num_kv_heads, int row_bytes, int block_size, int num_blocks,
+                              hipStream_t stream);
+
+hipError_t launch_compute_slots(int64_t *slot_mapping, const int32_t *block_tables,
+                                int max_blocks_per_seq, const int32_t *context_lens,
+                                const int32_t *seq_ids, const int32_t *positions,
+                                int num_tokens, int num_seqs, int block_size, int num_blocks,
+                                hipStream_t stream);
+
+}  // namespace pa

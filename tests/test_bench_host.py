@@ -1,0 +1,30 @@
+"""Host-side checks of bench.py's byte accounting (no GPU)."""
+import json
+import os
+
+import bench
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_kv_bytes_match_page2_formula():
+    """P2 section 2.2: LLaMA-7B (32 layers, 32 heads of 128, fp16) holds
+    1,073,741,824 bytes of K and V at 2048 tokens; one layer is 1/32 of it."""
+    with open(os.path.join(GOLDEN, "p2_kv_bytes.json")) as f:
+        g = json.load(f)
+    b = bench.algorithmic_bytes([g["seq_len"]], g["num_heads"], g["num_heads"], g["head_dim"], 16, "f16")
+    assert b["kv"] * g["num_layers"] == g["bytes"]
+
+
+def test_total_bytes_tiny_workload():
+    # 4 sequences {17, 50, 128, 200}, 8 heads of 64, fp32, B = 16
+    b = bench.algorithmic_bytes([17, 50, 128, 200], 8, 8, 64, 16, "f32")
+    assert b["kv"] == 395 * 8 * 64 * 4 * 2
+    assert b["q_out"] == 2 * 4 * 8 * 64 * 4
+    assert b["table"] == (2 + 4 + 8 + 13) * 4
+    assert b["total"] == 1_634_412
+
+
+def test_multi_gpu_request_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err

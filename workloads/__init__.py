@@ -282,3 +282,59 @@ def make_workload(index: int, seed: int | None = None, block_size: int | None = 
         return build(name, "f16", ctx, 32 // head_scale, 32 // head_scale, 128, block_size or 64, seed,
                      pool="permutation", shared_prefix_tokens=2048, partition_size=512)
     raise ValueError(index)
+
+
+# ---------------------------------------------------------------------------
+# Device copies (plumbing only: the raw words are moved, never converted)
+# ---------------------------------------------------------------------------
+
+def torch_dtype(dtype: str):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+
+
+def to_torch(raw: np.ndarray, dtype: str, device="cpu"):
+    """The raw storage words of ``raw`` as a torch tensor of the storage type."""
+    import torch
+    arr = np.ascontiguousarray(raw)
+    if dtype == "bf16":
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(arr)
+    return t.to(device)
+
+
+def from_torch(t, dtype: str) -> np.ndarray:
+    """Raw storage words of a torch tensor as numpy (bf16 as uint16)."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+@dataclass
+class DeviceWorkload:
+    q: object
+    key_cache: object
+    value_cache: object
+    block_tables: object
+    context_lens: object
+    new_key: object
+    new_value: object
+    out: object
+
+
+def to_device(wl: Workload, device="cuda") -> DeviceWorkload:
+    import torch
+    q = to_torch(wl.q, wl.dtype, device)
+    return DeviceWorkload(
+        q=q,
+        key_cache=to_torch(wl.key_cache, wl.dtype, device),
+        value_cache=to_torch(wl.value_cache, wl.dtype, device),
+        block_tables=torch.from_numpy(wl.block_tables).to(device),
+        context_lens=torch.from_numpy(wl.context_lens).to(device),
+        new_key=to_torch(wl.new_key, wl.dtype, device),
+        new_value=to_torch(wl.new_value, wl.dtype, device),
+        out=torch.empty_like(q),
+    )
