@@ -97,49 +97,62 @@ __device__ __forceinline__ void store_out(void *base, size_t elem, const float *
   }
 }
 
-template <int DT, int D>
-__global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
+template <int DT, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   using Sh = MhaShape<DT, D>;
   constexpr int E = Sh::kE, EPL = Sh::kEpl, LPT = Sh::kLpt, TPL = Sh::kTpl, NL = Sh::kLoads;
+  static_assert(NW * 64 >= kMaxPartBlocks, "one thread per staged block id");
 
   __shared__ int s_tbl[kMaxPartBlocks];
-  __shared__ float s_o[kWaves][D];
-  __shared__ float s_m[kWaves], s_l[kWaves];
+  __shared__ float s_o[NW][D];
+  __shared__ float s_m[NW], s_l[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
 
   const int H = a.num_heads, S = a.num_seqs;
+#if PA_XCD_REMAP
   const int item = xcd_logical_index(blockIdx.x, gridDim.x);
+#else
+  const int item = blockIdx.x;
+#endif
   const int h = item % H;
   const int s = (item / H) % S;
   const int p = item / (H * S);
-
+  const int G = H / a.num_kv_heads;
+  const int kvh = h / G;
+  const int row = lane / LPT;
+  const int col = lane % LPT;
   const int P = a.partition_size;
+  const int t0 = p * P;
+  const int b0 = t0 >> a.log2_block;
+  const size_t row_out = ((size_t)s * H + h) * D;
+
+  // Issue the three independent prologue loads together: the context length,
+  // this partition's window of the block table (every entry the window can
+  // hold that exists in the table, whatever the context turns out to be) and
+  // q, a 16-byte slice per lane (every row of the wave holds the same slice).
   const int ctx = a.context_lens[s];
+  const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks_per_seq + b0;
+  const int window = min(P >> a.log2_block, a.max_blocks_per_seq - b0);
+  const int id = tid < window ? trow[tid] : -1;
+  const u32x4 qv = *reinterpret_cast<const u32x4 *>(
+      reinterpret_cast<const char *>(a.q) + (row_out + col * EPL) * E);
+
   const bool bad_ctx = ctx < 0 || ctx > a.max_context_len ||
                        ctx > a.max_blocks_per_seq * a.block_size;
   const int nps = bad_ctx ? 1 : (ctx + P - 1) / P;
   if (p >= (nps > 0 ? nps : 1)) return;           // uniform over the work-group
   const bool direct = nps <= 1;
-
-  const int t0 = p * P;
   const int t1 = bad_ctx ? t0 : min(t0 + P, ctx);
-  const int b0 = t0 >> a.log2_block;
   const int nblk = bad_ctx ? 0 : ((t1 - t0 + a.block_size - 1) >> a.log2_block);
 
-  // Stage the partition's block ids; flag any id outside the pool.
-  bool bad_id = false;
-  const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks_per_seq + b0;
-  for (int i = tid; i < nblk; i += 256) {
-    const int id = trow[i];
-    bad_id |= (id < 0) | (id >= a.num_blocks);
-    s_tbl[i] = id;
-  }
+  // Stage the block ids in use; flag any outside the pool.
+  const bool bad_id = tid < nblk && (id < 0 || id >= a.num_blocks);
+  if (tid < nblk) s_tbl[tid] = id;
   const bool poison = __syncthreads_or(bad_id) || bad_ctx;
 
-  const size_t row_out = ((size_t)s * H + h) * D;
   const size_t part = ((size_t)s * H + h) * a.num_partitions + p;
   if (poison) {
     const float nan = __builtin_nanf("");
@@ -158,20 +171,11 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
     return;
   }
 
-  const int G = H / a.num_kv_heads;
-  const int kvh = h / G;
-  const int row = lane / LPT;
-  const int col = lane % LPT;
-
-  // q: every row of the wave holds the same 16-byte slice of q[s][h].
-  const u32x4 qv = *reinterpret_cast<const u32x4 *>(
-      reinterpret_cast<const char *>(a.q) + (row_out + col * EPL) * E);
-
   const int nch = (t1 - t0 + kChunk - 1) / kChunk;
-  const int nch_w = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;
-  // This wave's chunk k is partition chunk wave + 4k; lane k keeps its block id.
+  const int nch_w = nch > wave ? (nch - wave + NW - 1) / NW : 0;
+  // This wave's chunk k is partition chunk wave + NW*k; lane k keeps its block id.
   int my_ids = 0;
-  if (lane < nch_w) my_ids = s_tbl[((wave + kWaves * lane) * kChunk) >> a.log2_block];
+  if (lane < nch_w) my_ids = s_tbl[((wave + NW * lane) * kChunk) >> a.log2_block];
 
   const size_t head_stride = (size_t)a.block_size * D;        // elements per (block, head) tile
   const size_t block_stride = head_stride * a.num_kv_heads;
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   // Byte offset (from the kv head's first tile) of this wave's chunk k.
   auto chunk_offset = [&](int k) -> size_t {
     const int phys = __builtin_amdgcn_readlane(my_ids, k);
-    const int tok = (wave + kWaves * k) * kChunk;             // relative to t0, block aligned
+    const int tok = (wave + NW * k) * kChunk;                 // relative to t0, block aligned
     const int off = tok & (a.block_size - 1);
     return ((size_t)phys * block_stride + (size_t)off * D) * E;
   };
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   for (int i = 0; i < EPL; ++i) o[i] = 0.f;
 
   auto consume = [&](const u32x4 *kb, const u32x4 *vb, int k) {
-    const int tc = t0 + (wave + kWaves * k) * kChunk;
+    const int tc = t0 + (wave + NW * k) * kChunk;
     float sc[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) sc[j] = group_sum<LPT>(lane_dot<DT>(qv, kb[j])) * a.scale_log2;
@@ -246,19 +250,24 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
     m = mnew;
   };
 
-  // Two chunks per trip, each buffer reloaded right after it is consumed.
-  // The reload past the last chunk is clamped to it (an L2 hit, not used).
-  u32x4 kb0[NL], vb0[NL], kb1[NL], vb1[NL];
+  // Software pipeline over NBUF register buffers: while chunk k is consumed,
+  // chunks k+1 .. k+NBUF-1 are in flight.  Loads past the last chunk are
+  // clamped to it (L2 hits, never consumed).
+  constexpr int NBUF = kDecodeBuffers;
+  u32x4 kb[NBUF][NL], vb[NBUF][NL];
   if (nch_w > 0) {
-    load(kb0, vb0, 0);
-    int k = 0;
-    for (; k + 1 < nch_w; k += 2) {
-      load(kb1, vb1, k + 1);
-      consume(kb0, vb0, k);
-      load(kb0, vb0, min(k + 2, nch_w - 1));
-      consume(kb1, vb1, k + 1);
+    const int last = nch_w - 1;
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) load(kb[i], vb[i], min(i, last));
+    for (int k0 = 0; k0 < nch_w; k0 += NBUF) {
+#pragma unroll
+      for (int i = 0; i < NBUF; ++i) {
+        const int k = k0 + i;
+        if (k >= nch_w) break;
+        load(kb[(i + NBUF - 1) % NBUF], vb[(i + NBUF - 1) % NBUF], min(k + NBUF - 1, last));
+        consume(kb[i], vb[i], k);
+      }
     }
-    if (k < nch_w) consume(kb0, vb0, k);
   }
 
   // Merge the rows of this wave (lanes with equal col, different row).
@@ -288,15 +297,15 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // Merge the 4 waves; thread d < D owns output element d.
+  // Merge the NW waves; thread d < D owns output element d.
   if (tid < D) {
     float Mw = s_m[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) Mw = fmaxf(Mw, s_m[w]);
+    for (int w = 1; w < NW; ++w) Mw = fmaxf(Mw, s_m[w]);
     const float Ms = Mw == kNegInf ? 0.f : Mw;
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = exp2_fast(s_m[w] - Ms);
       L += f * s_l[w];
       O += f * s_o[w][tid];
@@ -321,7 +330,7 @@ template <int DT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;                  // output elements per lane
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int item = blockIdx.x * kMergeItems + (threadIdx.x >> 6);
   const int H = a.num_heads;
   if (item >= a.num_seqs * H) return;
   const int s = item / H;
@@ -369,13 +378,14 @@ template <int DT, int D>
 hipError_t launch_mha_t(const DecodeArgs &a, hipStream_t stream) {
   const long n = (long)a.num_seqs * a.num_heads * a.num_partitions;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_mha_kernel<DT, D>), dim3((unsigned)n), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_mha_kernel<DT, D, kDecodeWaves>), dim3((unsigned)n),
+                     dim3(kDecodeWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int DT, int D>
 hipError_t launch_merge_t(const DecodeArgs &a, hipStream_t stream) {
-  const long n = ((long)a.num_seqs * a.num_heads + kWaves - 1) / kWaves;
+  const long n = ((long)a.num_seqs * a.num_heads + kMergeItems - 1) / kMergeItems;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL((merge_kernel<DT, D>), dim3((unsigned)n), dim3(256), 0, stream, a);
   return hipGetLastError();

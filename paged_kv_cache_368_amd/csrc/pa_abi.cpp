@@ -29,9 +29,12 @@ int ilog2(int v) {
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-// Work-groups the auto choice aims for: enough to keep every CU of the chip
-// busy with several resident work-groups while short partitions stay rare.
-constexpr long long kTargetWorkgroups = 2048;
+// The automatic partition length.  Measured on MI355X: longer partitions are
+// faster (fewer work-group prologues, no merge pass when one partition covers
+// the context), so one partition per context up to 4096 tokens, 2048-token
+// partitions beyond that, shortened only while the grid would give fewer
+// than 4 work-groups per CU.
+constexpr long long kMinWorkgroups = 1024;
 
 struct Sizes {
   int partition;
@@ -74,8 +77,8 @@ pa_status_t plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
       return fail(PA_ERR_UNSUPPORTED, "partition_size above 4096 tokens is not supported");
   } else {
     const long long items = (long long)num_seqs * num_heads;
-    P = pa::kMaxPartition;
-    while (P > 256 && items * ceil_div(max_context_len, P) < kTargetWorkgroups) P /= 2;
+    P = max_context_len > pa::kMaxPartition ? pa::kMaxPartition / 2 : pa::kMaxPartition;
+    while (P > 256 && items * ceil_div(max_context_len, P) < kMinWorkgroups) P /= 2;
   }
   const long long np = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
   if ((long long)num_seqs * num_heads * np > 0x7fffffffLL)

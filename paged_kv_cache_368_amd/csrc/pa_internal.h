@@ -17,7 +17,18 @@ inline int elem_bytes(int dt) { return dt == kF32 ? 4 : 2; }
 // of the partition's table slice.
 constexpr int kMaxPartition = 4096;
 constexpr int kChunk = 16;            // tokens per inner-loop step of a wave
-constexpr int kWaves = 4;             // waves per work-group
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+constexpr int kDecodeWaves = PA_DECODE_WAVES;   // waves per decode work-group
+#ifndef PA_XCD_REMAP
+#define PA_XCD_REMAP 0
+#endif
+#ifndef PA_DECODE_BUFFERS
+#define PA_DECODE_BUFFERS 2
+#endif
+constexpr int kDecodeBuffers = PA_DECODE_BUFFERS; // K/V chunk buffers in flight per wave
+constexpr int kMergeItems = 4;                   // (sequence, head) rows per merge work-group
 constexpr int kMaxPartBlocks = kMaxPartition / 16;
 
 struct DecodeArgs {
