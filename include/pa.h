@@ -158,7 +158,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
  * max_blocks_per_seq * block_size, or whose used table entries fall outside
  * [0, num_blocks), gets NaN in every output element instead of a result.
  * Supported: head_dim in {64, 128}; block_size in {16, 32, 64};
- * num_heads % num_kv_heads == 0.
+ * num_heads % num_kv_heads == 0.  fp16/bf16 with 2 <= num_heads /
+ * num_kv_heads <= 16 run on the matrix cores (one work item per kv head);
+ * every other case runs on the vector units (one work item per query head).
  */
 pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const void *value_cache,
                       const int32_t *block_tables, const int32_t *context_lens,

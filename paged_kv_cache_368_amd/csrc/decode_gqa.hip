@@ -1,0 +1,379 @@
+// PagedAttention decode for grouped-query attention on the matrix cores
+// (gfx950), fp16 and bf16.
+//
+// Same result as the vector kernel (P1 §1 first formula over the context
+// gathered through the block table, P3 §2-§3), but the G query heads that
+// share a kv head are processed together: each K/V chunk is read once and
+// used by all G rows, which turns the per-chunk work into two small dense
+// products.
+//
+// Work decomposition: one work-group of NW waves per (sequence, kv head,
+// partition); waves take 16-token chunks round-robin.  Per chunk:
+//
+//   S^T[t][q] = sum_d K[t][d] Q[q][d]      v_mfma_f32_16x16x32  (D/32 of them)
+//   O[q][d]  += sum_t P[q][t] V[t][d]      v_mfma_f32_16x16x16  (D/16 tiles)
+//
+// with the 16 tokens of the chunk as the M (then K) dimension and up to 16
+// query heads as N (rows q >= G are zero padding).  The output layout of the
+// first product (lane l holds tokens 4*(l/16)..+3 of query l%16) is exactly
+// the A-operand layout of the second, so the probabilities never leave their
+// registers.  P is fed as two 16-bit halves (hi = truncated P, lo = the
+// remainder) so the product keeps ~16 significant bits of every weight; the
+// accumulation is fp32.
+//
+// Operand sourcing: K rows are loaded straight into the A layout (lane l:
+// token l%16, 16 bytes of dims); Q is loaded once into the B layout.  V is
+// needed with tokens along each lane (B layout of the second product), the
+// transpose of how it sits in the pool, so each chunk of V is loaded with
+// contiguous 1 KB wave loads, written to a per-wave LDS tile whose row pitch
+// is padded to D*2+8 bytes (the four token groups read by one instruction
+// fall in disjoint banks), and gathered back with 16-bit LDS reads.
+//
+// Online softmax per query column, with a lazy reference: the running max m
+// is only raised when a chunk's max exceeds it by more than 8 (log2 units),
+// so the rescale of O (which needs the factors moved from query-column lanes
+// to output-row lanes) is rare; unnormalised weights stay below 2^8, far
+// from fp32 or bf16 limits, and the final o/l is independent of the
+// reference chosen.
+#include "pa_device.h"
+
+namespace pa {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLazyMax = 8.f;          // log2 units: weights stay <= 256
+constexpr int kGMax = 16;                // query heads per kv head on one tile
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_k32(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_k16(const u32x2 &a, const u32x2 &b, const f32x4 &c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// Split two fp32 weights into packed 16-bit (hi, lo) words: hi keeps the top
+// bits (truncation, so p - hi is exact in fp32), lo the next ones.
+template <int DT>
+__device__ __forceinline__ void split2(float p0, float p1, uint32_t &hi, uint32_t &lo) {
+  if constexpr (DT == kBF16) {
+    const uint32_t b0 = __builtin_bit_cast(uint32_t, p0), b1 = __builtin_bit_cast(uint32_t, p1);
+    hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);                 // upper halves
+    const float r0 = p0 - __builtin_bit_cast(float, b0 & 0xffff0000u);
+    const float r1 = p1 - __builtin_bit_cast(float, b1 & 0xffff0000u);
+    lo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, r1), __builtin_bit_cast(uint32_t, r0),
+                               0x07060302u);
+  } else {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(p0, p1);     // round toward zero
+    const float h0 = (float)h.x, h1 = (float)h.y;
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0 - h0, p1 - h1));
+  }
+}
+
+template <int DT, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(DecodeArgs a) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(NW * 64 >= kMaxPartBlocks, "one thread per staged block id");
+  constexpr int E = 2;
+  constexpr int ROW = D * E;                 // bytes per token row
+  constexpr int PITCH = ROW + 8;             // LDS row pitch (bank spread)
+  constexpr int KI = D / 32;                 // first-product steps
+  constexpr int NT = D / 16;                 // output tiles of 16 dims
+  constexpr int LPT = ROW / 16;              // lanes per row for the V loads
+  constexpr int TPL = 64 / LPT;              // rows per V wave load
+  constexpr int VL = kChunk / TPL;           // V loads per chunk
+
+  __shared__ int s_tbl[kMaxPartBlocks];
+  // V tiles during the loop; reused for the cross-wave merge afterwards.
+  constexpr int kTileBytes = kChunk * PITCH;
+  constexpr int kMergeBytes = NW * kGMax * (D + 2) * 4;
+  constexpr int kLdsBytes = (NW * kTileBytes > kMergeBytes) ? NW * kTileBytes : kMergeBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char s_buf[kLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4;                  // lane group (0..3)
+  const int c16 = lane & 15;                 // lane within group
+
+  const int Hkv = a.num_kv_heads, S = a.num_seqs, H = a.num_heads;
+  const int G = H / Hkv;
+  const int item = blockIdx.x;
+  const int kvh = item % Hkv;
+  const int s = (item / Hkv) % S;
+  const int p = item / (Hkv * S);
+  const int P = a.partition_size;
+  const int t0 = p * P;
+  const int b0 = t0 >> a.log2_block;
+
+  // Prologue loads, issued together: context length, table window, and the
+  // Q fragments (B layout: lane l holds query l%16, dims 32i + 8*(l/16) ..+7).
+  const int ctx = a.context_lens[s];
+  const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks_per_seq + b0;
+  const int window = min(P >> a.log2_block, a.max_blocks_per_seq - b0);
+  const int id = tid < window ? trow[tid] : -1;
+  u32x4 qf[KI];
+  {
+    const bool live = c16 < G;
+    const char *qrow = reinterpret_cast<const char *>(a.q) +
+                       ((size_t)s * H + (size_t)kvh * G + (live ? c16 : 0)) * ROW;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(qrow + 64 * i + 16 * g4);
+      qf[i] = live ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const bool bad_ctx = ctx < 0 || ctx > a.max_context_len ||
+                       ctx > a.max_blocks_per_seq * a.block_size;
+  const int nps = bad_ctx ? 1 : (ctx + P - 1) / P;
+  if (p >= (nps > 0 ? nps : 1)) return;
+  const bool direct = nps <= 1;
+  const int t1 = bad_ctx ? t0 : min(t0 + P, ctx);
+  const int nblk = bad_ctx ? 0 : ((t1 - t0 + a.block_size - 1) >> a.log2_block);
+  const bool bad_id = tid < nblk && (id < 0 || id >= a.num_blocks);
+  if (tid < nblk) s_tbl[tid] = id;
+  const bool poison = __syncthreads_or(bad_id) || bad_ctx;
+
+  if (poison) {
+    const float nan = __builtin_nanf("");
+    for (int idx = tid; idx < G * D; idx += NW * 64) {
+      const int q = idx / D, d = idx - q * D;
+      const int h = kvh * G + q;
+      if (direct) {
+        store_out<DT>(a.out, ((size_t)s * H + h) * D + d, &nan, 1);
+      } else {
+        const size_t part = ((size_t)s * H + h) * a.num_partitions + p;
+        a.ws_o[part * D + d] = nan;
+        if (d == 0) {
+          a.ws_ml[2 * part] = __builtin_inff();
+          a.ws_ml[2 * part + 1] = nan;
+        }
+      }
+    }
+    return;
+  }
+
+  const int nch = (t1 - t0 + kChunk - 1) / kChunk;
+  const int nch_w = nch > wave ? (nch - wave + NW - 1) / NW : 0;
+  int my_ids = 0;
+  if (lane < nch_w) my_ids = s_tbl[((wave + NW * lane) * kChunk) >> a.log2_block];
+
+  const size_t head_stride = (size_t)a.block_size * D;
+  const size_t block_stride = head_stride * Hkv;
+  const char *kbase = reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E;
+  const char *vbase = reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E;
+  // K: lane l reads token l%16, bytes 64i + 16*(l/16) of its row (A layout).
+  const int k_off = c16 * ROW + 16 * g4;
+  // V: contiguous wave loads, lane l reads row (l/LPT) + TPL*j, bytes 16*(l%LPT).
+  const int v_row = lane / LPT, v_col = lane % LPT;
+  const int v_off = v_row * ROW + 16 * v_col;
+  constexpr int kChunkBytes = kChunk * ROW;
+
+  auto chunk_offset = [&](int k) -> size_t {
+    const int phys = __builtin_amdgcn_readlane(my_ids, k);
+    const int tok = (wave + NW * k) * kChunk;
+    const int off = tok & (a.block_size - 1);
+    return ((size_t)phys * block_stride + (size_t)off * D) * E;
+  };
+  auto load = [&](u32x4 *kb, u32x4 *vb, int k) {
+    const size_t off = chunk_offset(k);
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, kChunkBytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, kChunkBytes, kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) kb[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * i, 0, 0);
+#pragma unroll
+    for (int j = 0; j < VL; ++j)
+      vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, v_off + j * TPL * ROW, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  unsigned char *tile = s_buf + wave * kTileBytes;
+  float m = kNegInf;           // running reference max of query column c16
+  float l = 0.f;               // this lane's share of the column's weight sum
+  f32x4 o[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto consume = [&](const u32x4 *kb, const u32x4 *vb, int k) {
+    const int tc = t0 + (wave + NW * k) * kChunk;
+    const bool tail = tc + kChunk > t1;
+    // S^T for tokens 4*g4 + r of the chunk, query c16.
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KI; ++i) sacc = mfma_k32<DT>(kb[i], qf[i], sacc);
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = sacc[r] * a.scale_log2;
+      if (tail && tc + 4 * g4 + r >= t1) sc[r] = kNegInf;
+    }
+    float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    // Raise the reference only when the chunk max exceeds it by kLazyMax.
+    if (__builtin_amdgcn_ballot_w64(mloc > m + kLazyMax)) {
+      const float mnew = fmaxf(m, mloc);
+      const float corr = mnew == kNegInf ? 1.f : exp2_fast(m - mnew);
+      l *= corr;
+      // Output row q = 4*g4 + r needs the factor of query column q.
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float cr = __shfl(corr, 4 * g4 + r);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) o[n][r] *= cr;
+      }
+      m = mnew;
+    }
+    const float msafe = m == kNegInf ? 0.f : m;
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pw[r] = exp2_fast(sc[r] - msafe);
+      l += pw[r];
+    }
+    uint32_t h01, l01, h23, l23;
+    split2<DT>(pw[0], pw[1], h01, l01);
+    split2<DT>(pw[2], pw[3], h23, l23);
+    const u32x2 phi = {h01, h23}, plo = {l01, l23};
+
+    // V: stage the chunk in this wave's LDS tile (rows past the context are
+    // zeroed: whatever the slot holds must not meet a zero weight as NaN).
+#pragma unroll
+    for (int j = 0; j < VL; ++j) {
+      const int row = v_row + j * TPL;
+      u32x4 v = vb[j];
+      if (tail && tc + row >= t1) v = u32x4{0u, 0u, 0u, 0u};
+      u32x2 *dst = reinterpret_cast<u32x2 *>(tile + row * PITCH + 16 * v_col);
+      dst[0] = u32x2{v.x, v.y};
+      dst[1] = u32x2{v.z, v.w};
+    }
+    // B operand of tile n: lane l holds V[4*(l/16) + e][16n + l%16], e = 0..3.
+    const uint16_t *col = reinterpret_cast<const uint16_t *>(tile + 4 * g4 * PITCH) + c16;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const uint16_t *cp = col + 16 * n;
+      u32x2 vf;
+      vf.x = (uint32_t)cp[0] | ((uint32_t)cp[PITCH / 2] << 16);
+      vf.y = (uint32_t)cp[PITCH] | ((uint32_t)cp[3 * PITCH / 2] << 16);
+      o[n] = mfma_k16<DT>(phi, vf, o[n]);
+      o[n] = mfma_k16<DT>(plo, vf, o[n]);
+    }
+  };
+
+  constexpr int NBUF = 2;
+  u32x4 kb[NBUF][KI], vb[NBUF][VL];
+  if (nch_w > 0) {
+    const int last = nch_w - 1;
+    load(kb[0], vb[0], 0);
+    for (int k0 = 0; k0 < nch_w; k0 += NBUF) {
+#pragma unroll
+      for (int i = 0; i < NBUF; ++i) {
+        const int k = k0 + i;
+        if (k >= nch_w) break;
+        load(kb[(i + 1) % NBUF], vb[(i + 1) % NBUF], min(k + 1, last));
+        consume(kb[i], vb[i], k);
+      }
+    }
+  }
+
+  // Column sums over the four lane groups.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  // Cross-wave merge through LDS (the V tiles are dead now).
+  __syncthreads();
+  float *s_m = reinterpret_cast<float *>(s_buf);                // [NW][kGMax]
+  float *s_l = s_m + NW * kGMax;                                 // [NW][kGMax]
+  float *s_o = s_l + NW * kGMax;                                 // [NW][kGMax][D]
+  if (g4 == 0) {
+    s_m[wave * kGMax + c16] = m;
+    s_l[wave * kGMax + c16] = l;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int q = 4 * g4 + r;
+    if (q < G) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) s_o[(wave * kGMax + q) * D + 16 * n + c16] = o[n][r];
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += NW * 64) {
+    const int q = idx / D, d = idx - q * D;
+    float Mw = s_m[q];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) Mw = fmaxf(Mw, s_m[w * kGMax + q]);
+    const float Ms = Mw == kNegInf ? 0.f : Mw;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = exp2_fast(s_m[w * kGMax + q] - Ms);
+      L += f * s_l[w * kGMax + q];
+      O += f * s_o[(w * kGMax + q) * D + d];
+    }
+    const int h = kvh * G + q;
+    if (direct) {
+      const float r = L == 0.f ? 0.f : O / L;
+      store_out<DT>(a.out, ((size_t)s * H + h) * D + d, &r, 1);
+    } else {
+      const size_t part = ((size_t)s * H + h) * a.num_partitions + p;
+      a.ws_o[part * D + d] = O;
+      if (d == 0) {
+        a.ws_ml[2 * part] = Mw;
+        a.ws_ml[2 * part + 1] = L;
+      }
+    }
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_gqa_t(const DecodeArgs &a, hipStream_t stream) {
+  const long n = (long)a.num_seqs * a.num_kv_heads * a.num_partitions;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_gqa_kernel<DT, D, kGqaWaves>), dim3((unsigned)n), dim3(kGqaWaves * 64),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gqa_supported(int dt, int head_dim, int num_heads, int num_kv_heads) {
+  const int G = num_heads / num_kv_heads;
+  return (dt == kF16 || dt == kBF16) && (head_dim == 64 || head_dim == 128) && G >= 2 &&
+         G <= kGMax;
+}
+
+hipError_t launch_decode_gqa(const DecodeArgs &a, int dt, hipStream_t stream) {
+  switch (dt * 1000 + a.head_dim) {
+    case kF16 * 1000 + 64: return launch_gqa_t<kF16, 64>(a, stream);
+    case kF16 * 1000 + 128: return launch_gqa_t<kF16, 128>(a, stream);
+    case kBF16 * 1000 + 64: return launch_gqa_t<kBF16, 64>(a, stream);
+    case kBF16 * 1000 + 128: return launch_gqa_t<kBF16, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

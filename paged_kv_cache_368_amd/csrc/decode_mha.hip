@@ -85,18 +85,6 @@ __device__ __forceinline__ void lane_axpy(float *o, float p, const u32x4 &v) {
   }
 }
 
-template <int DT>
-__device__ __forceinline__ void store_out(void *base, size_t elem, const float *o, int n) {
-  if constexpr (DT == kF32) {
-    float *p = reinterpret_cast<float *>(base) + elem;
-    for (int i = 0; i < n; ++i) p[i] = o[i];
-  } else {
-    uint16_t *p = reinterpret_cast<uint16_t *>(base) + elem;
-    for (int i = 0; i < n; ++i)
-      p[i] = (uint16_t)(DT == kF16 ? f32_to_f16_bits(o[i]) : f32_to_bf16_bits(o[i]));
-  }
-}
-
 template <int DT, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   using Sh = MhaShape<DT, D>;

@@ -32,9 +32,9 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 // The automatic partition length.  Measured on MI355X: longer partitions are
 // faster (fewer work-group prologues, no merge pass when one partition covers
 // the context), so one partition per context up to 4096 tokens, 2048-token
-// partitions beyond that, shortened only while the grid would give fewer
-// than 4 work-groups per CU.
-constexpr long long kMinWorkgroups = 1024;
+// partitions beyond that, shortened only while the grid would leave CUs
+// without a work-group (256 CUs).
+constexpr long long kMinWorkgroups = 256;
 
 struct Sizes {
   int partition;
@@ -76,7 +76,10 @@ pa_status_t plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
     if (P > pa::kMaxPartition)
       return fail(PA_ERR_UNSUPPORTED, "partition_size above 4096 tokens is not supported");
   } else {
-    const long long items = (long long)num_seqs * num_heads;
+    // Work items are (sequence, query head) on the vector kernel and
+    // (sequence, kv head) on the matrix-core grouped-query kernel.
+    const bool gqa = pa::gqa_supported(dtype, head_dim, num_heads, num_kv_heads);
+    const long long items = (long long)num_seqs * (gqa ? num_kv_heads : num_heads);
     P = max_context_len > pa::kMaxPartition ? pa::kMaxPartition / 2 : pa::kMaxPartition;
     while (P > 256 && items * ceil_div(max_context_len, P) < kMinWorkgroups) P /= 2;
   }
@@ -227,7 +230,9 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
   a.partition_size = z.partition;
   a.num_partitions = z.num_partitions;
 
-  hipError_t e = pa::launch_decode_mha(a, dtype, stream);
+  hipError_t e = pa::gqa_supported(dtype, head_dim, num_heads, num_kv_heads)
+                     ? pa::launch_decode_gqa(a, dtype, stream)
+                     : pa::launch_decode_mha(a, dtype, stream);
   if (e == hipSuccess && z.num_partitions > 1) e = pa::launch_merge(a, dtype, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
   return PA_OK;

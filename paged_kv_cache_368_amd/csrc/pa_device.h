@@ -67,6 +67,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return b >> 16;
 }
 
+// Store n float32 values as storage words of type DT (nearest-even).
+template <int DT>
+__device__ __forceinline__ void store_out(void *base, size_t elem, const float *o, int n) {
+  if constexpr (DT == kF32) {
+    float *p = reinterpret_cast<float *>(base) + elem;
+    for (int i = 0; i < n; ++i) p[i] = o[i];
+  } else {
+    uint16_t *p = reinterpret_cast<uint16_t *>(base) + elem;
+    for (int i = 0; i < n; ++i)
+      p[i] = (uint16_t)(DT == kF16 ? f32_to_f16_bits(o[i]) : f32_to_bf16_bits(o[i]));
+  }
+}
+
 // ---- cross-lane ------------------------------------------------------------
 
 // DPP controls (gfx9 encoding).

@@ -28,7 +28,11 @@ constexpr int kDecodeWaves = PA_DECODE_WAVES;   // waves per decode work-group
 #define PA_DECODE_BUFFERS 2
 #endif
 constexpr int kDecodeBuffers = PA_DECODE_BUFFERS; // K/V chunk buffers in flight per wave
-constexpr int kMergeItems = 4;                   // (sequence, head) rows per merge work-group
+constexpr int kMergeItems = 4;
+#ifndef PA_GQA_WAVES
+#define PA_GQA_WAVES 4
+#endif
+constexpr int kGqaWaves = PA_GQA_WAVES;          // waves per grouped-query work-group                   // (sequence, head) rows per merge work-group
 constexpr int kMaxPartBlocks = kMaxPartition / 16;
 
 struct DecodeArgs {
@@ -49,6 +53,12 @@ struct DecodeArgs {
 
 hipError_t launch_decode_mha(const DecodeArgs &a, int dt, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs &a, int dt, hipStream_t stream);
+
+// Grouped-query decode on the matrix cores: fp16/bf16, head_dim 64 or 128,
+// 2 <= num_heads / num_kv_heads <= 16.  One work item per (sequence, kv head,
+// partition) instead of per query head.
+bool gqa_supported(int dt, int head_dim, int num_heads, int num_kv_heads);
+hipError_t launch_decode_gqa(const DecodeArgs &a, int dt, hipStream_t stream);
 
 hipError_t launch_cache_write(const void *key, const void *value, void *key_cache,
                               void *value_cache, const int64_t *slot_mapping, int num_tokens,

@@ -286,3 +286,34 @@ def test_decode_full_size_sampled(name, idx, B):
     ref = _oracle(wl, pairs)
     for s, h in pairs:
         _assert_close(got[s, h], ref[s, h], wl.dtype, f"{name} (s={s}, h={h})")
+
+
+# ---------------------------------------------------------------------------
+# grouped-query heads: matrix-core kernel for fp16/bf16 with 2 <= G <= 16,
+# the vector kernel otherwise
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (8, 2), (16, 2), (32, 2), (64, 2), (32, 32)])
+def test_decode_grouped_query(dtype, D, H, Hkv):
+    _say(f"gqa {dtype} D={D} H={H}/{Hkv}")
+    ctx = [1, 15, 16, 17, 100, 555, 1024, 2100]
+    wl = build("gqa", dtype, ctx, H, Hkv, D, 16, seed=50 + H + D, pool="choice", pool_factor=1.2)
+    ref = _oracle(wl)
+    for ps in (0, 16, 256):
+        got = _run_decode(wl, ps)
+        _assert_close(got, ref, dtype, f"gqa {dtype} D={D} H={H}/{Hkv} P={ps}")
+
+
+def test_decode_grouped_query_scores_spread_wide():
+    """Large scores (|q.k| scale up to ~40 in log2 units) force the lazy
+    reference max to move several times inside one context."""
+    _say("gqa wide scores")
+    wl = build("gqa_wide", "bf16", [700, 1500, 64], 16, 2, 128, 16, seed=60, pool="permutation")
+    wl.q = (P.to_f64(wl.q, "bf16") * 6.0).astype(np.float32).view(np.uint32)
+    wl.q = (wl.q >> 16).astype(np.uint16)
+    ref = _oracle(wl)
+    for ps in (0, 64):
+        got = _run_decode(wl, ps)
+        _assert_close(got, ref, "bf16", f"gqa wide P={ps}")
