@@ -38,6 +38,22 @@ HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 
+# HBM traffic of one pa_decode call, from two rocprofv3 --pmc runs of this
+# script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, summed over the
+# kernels of the call), each scaled by what the same counter reads for a
+# plain 1 GiB device copy in the same run (FETCH_SIZE reads 524,310 KiB for
+# the copy's 1,048,576 KiB of reads: factor 1.99992; WRITE_SIZE reads the
+# copy's writes exactly: factor 1.0).  An entry holds only for the kernel
+# sources it was taken on (``sources`` = kernel_source_digest()); any change
+# to them reports traffic as null until the counters are taken again.
+COUNTERS = {
+    "llama7b_f16/B16/P4096": {
+        "sources": "025e9042c0c4ce6599e191b107b7c2e5105afa9ab0bfc125181a498ca27cf191",
+        "fetch_kib": 328458.703, "fetch_scale": 1.99992,
+        "write_kib": 256.0, "write_scale": 1.0,
+        "profile": "profiles/decode_mha_llama7b_f16.md"},
+}
+
 
 def algorithmic_bytes(context_lens, num_heads, num_kv_heads, head_dim, block_size, dtype) -> dict:
     """Bytes a decode launch must move at minimum: K and V rows of every
@@ -51,6 +67,28 @@ def algorithmic_bytes(context_lens, num_heads, num_kv_heads, head_dim, block_siz
     qo = 2 * len(ctx) * num_heads * head_dim * e
     table = sum(-(-c // block_size) for c in ctx) * 4
     return {"kv": kv, "q_out": qo, "table": table, "total": kv + qo + table}
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP/C++ sources and build flags of libpa.so."""
+    import hashlib
+    pkg = os.path.join(ROOT, "paged_kv_cache_368_amd")
+    csrc = os.path.join(pkg, "csrc")
+    h = hashlib.sha256()
+    for path in sorted(os.path.join(csrc, f) for f in os.listdir(csrc)) + [os.path.join(pkg, "build.py")]:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, block_size: int, partition_size: int):
+    """HBM bytes per pa_decode call from the stored counters, or None when
+    none were taken for this workload on the current kernel sources."""
+    c = COUNTERS.get(f"{workload}/B{block_size}/P{partition_size}")
+    if c is None or c["sources"] != kernel_source_digest():
+        return None
+    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024
 
 
 def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
@@ -208,7 +246,8 @@ def main(argv=None) -> int:
                    "max_context_len": maxctx, "partition_size": P_used, "seed": wl.seed,
                    "pool_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(wl.name, B, P_used),
                      "kernel": "pa_decode (decode kernel + merge pass when split)",
                      "bytes_per_launch": nbytes["total"], "mean_launch_us": dec_mean_s * 1e6,
                      "median_launch_us": dec_med_s * 1e6},
