@@ -203,10 +203,10 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(DecodeArgs a) {
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, kChunkBytes, kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < KI; ++i) kb[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * i, 0, 0);
+    for (int i = 0; i < KI; ++i) kb[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * i, 0, kStreamPolicy);
 #pragma unroll
     for (int j = 0; j < VL; ++j)
-      vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, v_off + j * TPL * ROW, 0, 0);
+      vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, v_off + j * TPL * ROW, 0, kStreamPolicy);
     __builtin_amdgcn_sched_barrier(0);
   };
 

@@ -192,10 +192,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, kChunkBytes, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < NL; ++j)
-      kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + j * TPL * D * E, 0, 0);
+      kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + j * TPL * D * E, 0, kStreamPolicy);
 #pragma unroll
     for (int j = 0; j < NL; ++j)
-      vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + j * TPL * D * E, 0, 0);
+      vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + j * TPL * D * E, 0, kStreamPolicy);
     // Keep the scheduler from sinking these loads below the compute that
     // follows: they must be in flight while the previous chunk is consumed.
     __builtin_amdgcn_sched_barrier(0);

@@ -125,6 +125,13 @@ __device__ __forceinline__ int xcd_logical_index(int hw_id, int n) {
 // Word 3 of a raw (untyped, unswizzled) buffer descriptor on CDNA3/CDNA4.
 constexpr int kBufferFlags = 0x00020000;
 
+// Cache-policy operand of the K/V buffer loads: the non-temporal bit (bit 1,
+// "nt" on gfx940-family targets).  K/V rows are read exactly once per call,
+// so they are marked as streaming; on MI355X this lifts a plain read of 4 KB
+// tiles in random order from ~5.8 to ~6.5 TB/s at 672 MB and from ~6.1 to
+// ~6.8 TB/s at 2.7 GB.
+constexpr int kStreamPolicy = 2;
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace pa
