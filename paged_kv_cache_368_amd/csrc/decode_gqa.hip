@@ -90,13 +90,15 @@ __device__ __forceinline__ void split2(float p0, float p1, uint32_t &hi, uint32_
   }
 }
 
+// Three waves per SIMD fit without spilling at head_dim 128 (153 VGPRs).
 template <int DT, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_gqa_kernel(DecodeArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(NW * 64 >= kMaxPartBlocks, "one thread per staged block id");
   constexpr int E = 2;
   constexpr int ROW = D * E;                 // bytes per token row
-  constexpr int PITCH = ROW + 8;             // LDS row pitch (bank spread)
+  constexpr int PITCH = ROW + 32;            // LDS row pitch: 16-byte rows, spread banks
   constexpr int KI = D / 32;                 // first-product steps
   constexpr int NT = D / 16;                 // output tiles of 16 dims
   constexpr int LPT = ROW / 16;              // lanes per row for the V loads
@@ -104,10 +106,12 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int VL = kChunk / TPL;           // V loads per chunk
 
   __shared__ int s_tbl[kMaxPartBlocks];
-  // V tiles during the loop; reused for the cross-wave merge afterwards.
+  // K and V tiles (one pair per wave) during the loop; reused for the
+  // cross-wave merge afterwards.
   constexpr int kTileBytes = kChunk * PITCH;
   constexpr int kMergeBytes = NW * kGMax * (D + 2) * 4;
-  constexpr int kLdsBytes = (NW * kTileBytes > kMergeBytes) ? NW * kTileBytes : kMergeBytes;
+  constexpr int kLdsBytes =
+      (2 * NW * kTileBytes > kMergeBytes) ? 2 * NW * kTileBytes : kMergeBytes;
   __shared__ __attribute__((aligned(16))) unsigned char s_buf[kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -183,9 +187,8 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(DecodeArgs a) {
   const size_t block_stride = head_stride * Hkv;
   const char *kbase = reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E;
   const char *vbase = reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E;
-  // K: lane l reads token l%16, bytes 64i + 16*(l/16) of its row (A layout).
-  const int k_off = c16 * ROW + 16 * g4;
-  // V: contiguous wave loads, lane l reads row (l/LPT) + TPL*j, bytes 16*(l%LPT).
+  // K and V: contiguous wave loads (every load instruction reads whole 1 KB
+  // of the chunk), lane l reads row (l/LPT) + TPL*j, bytes 16*(l%LPT).
   const int v_row = lane / LPT, v_col = lane % LPT;
   const int v_off = v_row * ROW + 16 * v_col;
   constexpr int kChunkBytes = kChunk * ROW;
@@ -203,14 +206,21 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(DecodeArgs a) {
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, kChunkBytes, kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < KI; ++i) kb[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * i, 0, kStreamPolicy);
+    for (int j = 0; j < VL; ++j)
+      kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, v_off + j * TPL * ROW, 0, kStreamPolicy);
 #pragma unroll
     for (int j = 0; j < VL; ++j)
       vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, v_off + j * TPL * ROW, 0, kStreamPolicy);
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  unsigned char *tile = s_buf + wave * kTileBytes;
+  unsigned char *ktile = s_buf + wave * 2 * kTileBytes;
+  unsigned char *tile = ktile + kTileBytes;
+  // Transposed-read addresses: for tile n, lane (g4, c16) points at row
+  // 4*g4 + c16/4, dims 16n + 4*(c16%4) .. +3; ds_read_b64_tr_b16 then hands
+  // lane (g4, c16) the four values V[4*g4 + e][16n + c16], e = 0..3, which is
+  // the B operand of the second product.
+  const unsigned char *tr_base = tile + (4 * g4 + c16 / 4) * PITCH + 8 * (c16 % 4);
   float m = kNegInf;           // running reference max of query column c16
   float l = 0.f;               // this lane's share of the column's weight sum
   f32x4 o[NT];
@@ -219,23 +229,49 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(DecodeArgs a) {
 
   auto consume = [&](const u32x4 *kb, const u32x4 *vb, int k) {
     const int tc = t0 + (wave + NW * k) * kChunk;
-    const bool tail = tc + kChunk > t1;
+    const bool tail = tc + kChunk > t1;                  // wave-uniform
+    // K: through this wave's LDS tile into the A layout (lane l: token l%16,
+    // bytes 64i + 16*(l/16) of its row).  Rows past the context are left as
+    // they are: their scores are replaced by -inf below, by select.
+#pragma unroll
+    for (int j = 0; j < VL; ++j)
+      *reinterpret_cast<u32x4 *>(ktile + (v_row + j * TPL) * PITCH + 16 * v_col) = kb[j];
+    u32x4 ka[KI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      ka[i] = *reinterpret_cast<const u32x4 *>(ktile + c16 * PITCH + 64 * i + 16 * g4);
     // S^T for tokens 4*g4 + r of the chunk, query c16.
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < KI; ++i) sacc = mfma_k32<DT>(kb[i], qf[i], sacc);
+    for (int i = 0; i < KI; ++i) sacc = mfma_k32<DT>(ka[i], qf[i], sacc);
     float sc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc[r] = sacc[r] * a.scale_log2;
-      if (tail && tc + 4 * g4 + r >= t1) sc[r] = kNegInf;
+    for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * a.scale_log2;
+    u32x4 vr[VL];
+#pragma unroll
+    for (int j = 0; j < VL; ++j) vr[j] = vb[j];
+    if (tail) {
+      // Tokens past the context: score -inf, V row zeroed (whatever the slot
+      // holds must not meet a zero weight as NaN).
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (tc + 4 * g4 + r >= t1) sc[r] = kNegInf;
+#pragma unroll
+      for (int j = 0; j < VL; ++j)
+        if (tc + v_row + j * TPL >= t1) vr[j] = u32x4{0u, 0u, 0u, 0u};
     }
-    float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // Raise the reference only when the chunk max exceeds it by kLazyMax.
+    // V: stage the chunk in this wave's LDS tile.
+#pragma unroll
+    for (int j = 0; j < VL; ++j)
+      *reinterpret_cast<u32x4 *>(tile + (v_row + j * TPL) * PITCH + 16 * v_col) = vr[j];
+
+    // Raise the reference only when some score exceeds it by kLazyMax: every
+    // lane of a query column holds the column's m, so the test needs no
+    // cross-lane traffic; the column max is formed only on that rare path.
+    const float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     if (__builtin_amdgcn_ballot_w64(mloc > m + kLazyMax)) {
-      const float mnew = fmaxf(m, mloc);
+      const float cm = max_xor32(max_xor16(mloc));
+      const float mnew = fmaxf(m, cm);
       const float corr = mnew == kNegInf ? 1.f : exp2_fast(m - mnew);
       l *= corr;
       // Output row q = 4*g4 + r needs the factor of query column q.
@@ -259,32 +295,18 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(DecodeArgs a) {
     split2<DT>(pw[2], pw[3], h23, l23);
     const u32x2 phi = {h01, h23}, plo = {l01, l23};
 
-    // V: stage the chunk in this wave's LDS tile (rows past the context are
-    // zeroed: whatever the slot holds must not meet a zero weight as NaN).
-#pragma unroll
-    for (int j = 0; j < VL; ++j) {
-      const int row = v_row + j * TPL;
-      u32x4 v = vb[j];
-      if (tail && tc + row >= t1) v = u32x4{0u, 0u, 0u, 0u};
-      u32x2 *dst = reinterpret_cast<u32x2 *>(tile + row * PITCH + 16 * v_col);
-      dst[0] = u32x2{v.x, v.y};
-      dst[1] = u32x2{v.z, v.w};
-    }
-    // B operand of tile n: lane l holds V[4*(l/16) + e][16n + l%16], e = 0..3.
-    const uint16_t *col = reinterpret_cast<const uint16_t *>(tile + 4 * g4 * PITCH) + c16;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const uint16_t *cp = col + 16 * n;
-      u32x2 vf;
-      vf.x = (uint32_t)cp[0] | ((uint32_t)cp[PITCH / 2] << 16);
-      vf.y = (uint32_t)cp[PITCH] | ((uint32_t)cp[3 * PITCH / 2] << 16);
+      const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(tr_base + 32 * n));
+      const u32x2 vf = __builtin_bit_cast(u32x2, t);
       o[n] = mfma_k16<DT>(phi, vf, o[n]);
       o[n] = mfma_k16<DT>(plo, vf, o[n]);
     }
   };
 
   constexpr int NBUF = 2;
-  u32x4 kb[NBUF][KI], vb[NBUF][VL];
+  u32x4 kb[NBUF][VL], vb[NBUF][VL];
   if (nch_w > 0) {
     const int last = nch_w - 1;
     load(kb[0], vb[0], 0);
@@ -300,8 +322,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(DecodeArgs a) {
   }
 
   // Column sums over the four lane groups.
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = sum_xor32(sum_xor16(l));
 
   // Cross-wave merge through LDS (the V tiles are dead now).
   __syncthreads();

@@ -110,6 +110,30 @@ template <int N> __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Combine each lane's value with that of lane l ^ 16 (or l ^ 32) through the
+// gfx950 permlane swaps, which stay in the VALU (no LDS round trip).  With
+// both operands equal, the two results of a swap are x[l] and x[l ^ 16] (x[l ^
+// 32]) in an order that depends on the lane, so only symmetric combinations
+// (sum, max) are formed; a + b is exact-order-independent in IEEE arithmetic.
+__device__ __forceinline__ void swap16(float x, float &a, float &b) {
+  const uint32_t w = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  a = as_f32(r0);
+  b = as_f32(r1);
+}
+__device__ __forceinline__ void swap32(float x, float &a, float &b) {
+  const uint32_t w = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  a = as_f32(r0);
+  b = as_f32(r1);
+}
+__device__ __forceinline__ float sum_xor16(float x) { float a, b; swap16(x, a, b); return a + b; }
+__device__ __forceinline__ float sum_xor32(float x) { float a, b; swap32(x, a, b); return a + b; }
+__device__ __forceinline__ float max_xor16(float x) { float a, b; swap16(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float max_xor32(float x) { float a, b; swap32(x, a, b); return fmaxf(a, b); }
+
 // ---- work-group order --------------------------------------------------------
 
 // Work-groups are handed to the 8 XCDs round-robin by hardware id.  Return a
