@@ -311,55 +311,91 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   }
 }
 
-// Log-sum-exp merge of split-context partitions: one wave per (s, h).
+// Log-sum-exp merge of split-context partitions: one work-group of four
+// waves per (s, h).
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
-// Sequences that fit one partition were written directly and are skipped.
+// Wave w takes partitions w, w + 4, ... in batches of kMergeBatch whose loads
+// are all issued before any is used, keeping its own running (max, sum,
+// output) with the same rescaling as the decode loop; the four waves are
+// combined through LDS.  Sequences that fit one partition were written
+// directly by the decode kernel and are skipped.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 8;
+
 template <int DT, int D>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;                  // output elements per lane
+  __shared__ float s_o[kMergeWaves][D];
+  __shared__ float s_m[kMergeWaves], s_l[kMergeWaves];
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * kMergeItems + (threadIdx.x >> 6);
-  const int H = a.num_heads;
-  if (item >= a.num_seqs * H) return;
-  const int s = item / H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x;                 // s * H + h
+  const int s = item / a.num_heads;
   const int ctx = a.context_lens[s];
   const int P = a.partition_size;
   if (ctx < 0 || ctx > a.max_context_len || ctx > a.max_blocks_per_seq * a.block_size) return;
   const int nps = (ctx + P - 1) / P;
-  if (nps <= 1) return;
+  if (nps <= 1) return;                        // uniform over the work-group
 
   const size_t base = (size_t)item * a.num_partitions;
-  float M = kNegInf;
-  for (int p = lane; p < nps; p += 64) M = fmaxf(M, a.ws_ml[2 * (base + p)]);
+  float m = kNegInf, l = 0.f;
+  float o[PER];
 #pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk));
-  const float Ms = M == kNegInf ? 0.f : M;
-
-  float L = 0.f;
-  float O[PER];
+  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  for (int p0 = wave; p0 < nps; p0 += kMergeWaves * kMergeBatch) {
+    float mp[kMergeBatch], lp[kMergeBatch], op[kMergeBatch][PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) O[i] = 0.f;
-  for (int p0 = 0; p0 < nps; p0 += 64) {
-    const int p = p0 + lane;
-    float f = 0.f;
-    if (p < nps) {
-      f = exp2_fast(a.ws_ml[2 * (base + p)] - Ms);
-      L += f * a.ws_ml[2 * (base + p) + 1];
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int p = min(p0 + u * kMergeWaves, nps - 1);   // clamped loads are never used
+      mp[u] = a.ws_ml[2 * (base + p)];
+      lp[u] = a.ws_ml[2 * (base + p) + 1];
+      const float *src = a.ws_o + (base + p) * D + lane * PER;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) op[u][i] = src[i];
     }
-    const int n = min(64, nps - p0);
-    for (int j = 0; j < n; ++j) {
-      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
-      const float *src = a.ws_o + (base + p0 + j) * D + lane * PER;
+    float mb = m;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) O[i] = __builtin_fmaf(fj, src[i], O[i]);
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (p0 + u * kMergeWaves < nps) mb = fmaxf(mb, mp[u]);
+    const float ms = mb == kNegInf ? 0.f : mb;
+    const float c = exp2_fast(m - ms);
+    l *= c;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] *= c;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      if (p0 + u * kMergeWaves < nps) {
+        const float f = exp2_fast(mp[u] - ms);
+        l = __builtin_fmaf(f, lp[u], l);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[i] = __builtin_fmaf(f, op[u][i], o[i]);
+      }
     }
+    m = mb;
   }
 #pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) L += __shfl_xor(L, msk);
-  float r[PER];
+  for (int i = 0; i < PER; ++i) s_o[wave][lane * PER + i] = o[i];
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_l[wave] = l;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    float Mw = s_m[0];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) r[i] = L == 0.f ? 0.f : O[i] / L;
-  store_out<DT>(a.out, (size_t)item * D + lane * PER, r, PER);
+    for (int w = 1; w < kMergeWaves; ++w) Mw = fmaxf(Mw, s_m[w]);
+    const float Ms = Mw == kNegInf ? 0.f : Mw;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+      const float f = exp2_fast(s_m[w] - Ms);
+      L += f * s_l[w];
+      O += f * s_o[w][d];
+    }
+    const float r = L == 0.f ? 0.f : O / L;    // NaN (a poisoned partition) propagates
+    store_out<DT>(a.out, (size_t)item * D + d, &r, 1);
+  }
 }
 
 template <int DT, int D>
@@ -373,9 +409,9 @@ hipError_t launch_mha_t(const DecodeArgs &a, hipStream_t stream) {
 
 template <int DT, int D>
 hipError_t launch_merge_t(const DecodeArgs &a, hipStream_t stream) {
-  const long n = ((long)a.num_seqs * a.num_heads + kMergeItems - 1) / kMergeItems;
+  const long n = (long)a.num_seqs * a.num_heads;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3((unsigned)n), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3((unsigned)n), dim3(kMergeWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 

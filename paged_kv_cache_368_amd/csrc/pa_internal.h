@@ -28,11 +28,10 @@ constexpr int kDecodeWaves = PA_DECODE_WAVES;   // waves per decode work-group
 #define PA_DECODE_BUFFERS 2
 #endif
 constexpr int kDecodeBuffers = PA_DECODE_BUFFERS; // K/V chunk buffers in flight per wave
-constexpr int kMergeItems = 4;
 #ifndef PA_GQA_WAVES
 #define PA_GQA_WAVES 4
 #endif
-constexpr int kGqaWaves = PA_GQA_WAVES;          // waves per grouped-query work-group                   // (sequence, head) rows per merge work-group
+constexpr int kGqaWaves = PA_GQA_WAVES;          // waves per grouped-query work-group
 constexpr int kMaxPartBlocks = kMaxPartition / 16;
 
 struct DecodeArgs {
