@@ -53,7 +53,10 @@ typedef enum {
   PA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, H % Hkv != 0, ... */
   PA_ERR_UNSUPPORTED = 2,        /* valid but not built: head_dim, block_size, dtype */
   PA_ERR_WORKSPACE_TOO_SMALL = 3,
-  PA_ERR_HIP = 4                 /* the HIP runtime refused the launch */
+  PA_ERR_HIP = 4,                /* the HIP runtime refused the launch */
+  PA_ERR_NO_BLOCKS = 5,          /* block manager: not enough free blocks */
+  PA_ERR_UNKNOWN_REQUEST = 6,    /* block manager: no table for this request id */
+  PA_ERR_STATE = 7               /* block manager: operation invalid in this state */
 } pa_status_t;
 
 /*

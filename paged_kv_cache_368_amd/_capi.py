@@ -19,7 +19,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
 
-PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP = range(5)
+(PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP,
+ PA_ERR_NO_BLOCKS, PA_ERR_UNKNOWN_REQUEST, PA_ERR_STATE) = range(8)
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 _lib = None
@@ -58,17 +59,45 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_last_error.restype = c.c_char_p
     lib.pa_version.argtypes = []
     lib.pa_version.restype = c.c_char_p
+    # host block manager (include/pa_blocks.h)
+    u64 = c.c_uint64
+    for name, args in {
+        "pa_bm_create": [i32, i32, ptr],
+        "pa_bm_allocate": [ptr, u64, i32, ptr],
+        "pa_bm_append_slot": [ptr, u64, i32, ptr, ptr, ptr, ptr],
+        "pa_bm_append_slots": [ptr, ptr, ptr, i32, ptr, ptr, ptr, ptr],
+        "pa_bm_share_prefix": [ptr, u64, u64, i32],
+        "pa_bm_fork": [ptr, u64, u64],
+        "pa_bm_free_request": [ptr, u64],
+        "pa_bm_stats": [ptr, ptr, ptr, ptr],
+        "pa_bm_table": [ptr, u64, ptr, i32, ptr],
+        "pa_bm_free_ids": [ptr, ptr, i32, ptr],
+        "pa_bm_fill_tables": [ptr, ptr, i32, i32, ptr],
+    }.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = st
+    lib.pa_bm_destroy.argtypes = [ptr]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_ref_count.argtypes = [ptr, i32]
+    lib.pa_bm_ref_count.restype = i32
     if path is None:
         _lib = lib
     return lib
 
 
-def declared_functions(header: str = HEADER) -> list[str]:
-    """Names of the functions include/pa.h declares."""
-    with open(header) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+def declared_functions(headers=None) -> list[str]:
+    """Names of the functions the headers under include/ declare."""
+    if headers is None:
+        inc = os.path.dirname(HEADER)
+        headers = [os.path.join(inc, f) for f in sorted(os.listdir(inc)) if f.endswith(".h")]
+    names = set()
+    for header in headers:
+        with open(header) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def _check(status: int) -> None:

@@ -100,6 +100,8 @@ pa_status_t plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
 
 }  // namespace
 
+pa_status_t pa::set_error(pa_status_t st, const char *msg) { return fail(st, msg); }
+
 extern "C" {
 
 const char *pa_last_error(void) { return g_last_error.c_str(); }

@@ -6,7 +6,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
+
+// Record the thread's last error text (read back by pa_last_error) and
+// return `st`.  Defined in pa_abi.cpp.
+pa_status_t set_error(pa_status_t st, const char *msg);
 
 enum Dt : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
