@@ -173,6 +173,35 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
                       int32_t partition_size, void *workspace, size_t workspace_bytes,
                       pa_dtype_t dtype, hipStream_t stream);
 
+/*
+ * pa_copy_blocks -- copy whole physical blocks from one pair of pools to
+ * another, for copy on write inside a pool (P3 §4: a beam fork shares block
+ * references; a request that writes into a shared block needs its own copy,
+ * see pa_blocks.h) and for swapping a preempted request's blocks out to host
+ * memory and back in (P3 §3, §5: blocks of low-priority requests move to CPU
+ * memory and return when GPU blocks are free).  A bit-exact copy:
+ *
+ *   dst_k[dst] = src_k[src],  dst_v[dst] = src_v[src]   for each pair
+ *
+ *   dst_k, dst_v     out  pools of dst_num_blocks blocks of block_bytes each
+ *   src_k, src_v     in   pools of src_num_blocks blocks of block_bytes each
+ *                         (dst_v and src_v may both be NULL: one pool only)
+ *   block_pairs      in   DEVICE int32 [num_pairs][2] = (src block, dst block)
+ *   block_bytes           bytes of one physical block (num_kv_heads *
+ *                         block_size * head_dim * element bytes for the
+ *                         layouts of pa_decode); a multiple of 16
+ *
+ * Every pool pointer is device memory, or pinned host memory from
+ * hipHostMalloc (mapped into the device address space: the kernel then
+ * reads or writes across the host link).  Pools must be 16-byte aligned.  A
+ * pair whose src or dst is outside its pool is skipped.  Pairs are copied in
+ * no particular order: a block that is the dst of one pair and the src of
+ * another in the same call gives an unspecified result.
+ */
+pa_status_t pa_copy_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
+                           const int32_t *block_pairs, int32_t num_pairs, int64_t block_bytes,
+                           int32_t dst_num_blocks, int32_t src_num_blocks, hipStream_t stream);
+
 /* Text of the last non-OK status returned on the calling thread. */
 const char *pa_last_error(void);
 

@@ -80,6 +80,22 @@ def compute_slots(block_tables, block_size: int, num_blocks: int, context_lens=N
 
 
 # ---------------------------------------------------------------------------
+# Whole-block copies -- P3 §4 (a beam fork shares block references; a writer
+# into a shared block needs a private copy) and P3 §3, §5 (blocks of a
+# preempted request are swapped out to CPU memory and back in).
+# ---------------------------------------------------------------------------
+
+def copy_blocks(dst_pool, src_pool, pairs) -> None:
+    """``dst_pool[d] = src_pool[s]`` bit for bit for each (s, d) pair whose ids
+    lie inside their pools; other pairs are skipped.  Pools are arrays whose
+    first axis is the physical block id."""
+    for s_id, d_id in pairs:
+        s_id, d_id = int(s_id), int(d_id)
+        if 0 <= s_id < src_pool.shape[0] and 0 <= d_id < dst_pool.shape[0]:
+            dst_pool[d_id] = src_pool[s_id]
+
+
+# ---------------------------------------------------------------------------
 # Storage decoding
 # ---------------------------------------------------------------------------
 

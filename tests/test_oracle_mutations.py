@@ -99,7 +99,17 @@ def _kv_bytes_no_two(seq_len, layers, heads, hd, e):
     return seq_len * layers * heads * hd * e
 
 
+def _copy_reversed(dst_pool, src_pool, pairs):
+    return _orig["copy_blocks"](dst_pool, src_pool, [(d, s) for s, d in pairs])
+
+
+def _copy_no_bounds(dst_pool, src_pool, pairs):
+    for s, d in pairs:
+        dst_pool[int(d) % dst_pool.shape[0]] = src_pool[int(s) % src_pool.shape[0]]
+
+
 MUTANTS = {
+    "copy_blocks": [_copy_reversed, _copy_no_bounds],
     "num_required_blocks": [_floor_blocks],
     "physical_location": [_swapped_location, _off_by_one_location],
     "attention": [_no_scale, _wrong_sign, _mean_normaliser, _keys_as_values, _blockwise],

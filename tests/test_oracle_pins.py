@@ -378,3 +378,46 @@ def test_workload_reproducible_and_prefix_shared():
     b = build("t", "bf16", [70, 130], 4, 2, 16, 16, seed=3, shared_prefix_tokens=32)
     assert np.array_equal(a.key_cache, b.key_cache) and np.array_equal(a.block_tables, b.block_tables)
     assert np.array_equal(a.block_tables[0, :2], a.block_tables[1, :2])
+
+
+# --------------------------------------------------------------------------
+# Whole-block copies (swap out / in, copy on write)
+# --------------------------------------------------------------------------
+
+def test_pin_copy_blocks_swap_round_trip_keeps_attention():
+    """Swapping a request's blocks out to a host pool and back in to other
+    device blocks (P3 §3, §5), with its table rewritten to the new ids, leaves
+    the pool contents it reads -- and so its attention output -- bit for bit
+    unchanged; blocks named by no pair are untouched; out-of-range pairs are
+    skipped."""
+    rng = _rng(31)
+    NB, Hkv, B, D, n = 12, 2, 4, 8, 13
+    kc = rng.standard_normal((NB, Hkv, B, D)).astype(np.float32)
+    vc = rng.standard_normal((NB, Hkv, B, D)).astype(np.float32)
+    table = [7, 2, 9, 4]
+    q = rng.standard_normal((1, Hkv, D)).astype(np.float32)
+    before = P.paged_decode(q, kc, vc, np.array([table], np.int32), np.array([n], np.int32), B,
+                            0.3, "f32")
+    host_k = np.full((6, Hkv, B, D), -7.0, np.float32)
+    host_v = np.full((6, Hkv, B, D), -7.0, np.float32)
+    out_pairs = [(b, i) for i, b in enumerate(table)] + [(99, 0), (0, 99)]
+    P.copy_blocks(host_k, kc, out_pairs)
+    P.copy_blocks(host_v, vc, out_pairs)
+    for i, b in enumerate(table):
+        assert host_k[i].tobytes() == kc[b].tobytes() and host_v[i].tobytes() == vc[b].tobytes()
+    assert (host_k[4:] == -7.0).all() and (host_v[4:] == -7.0).all()
+    # the request's device blocks are reused by someone else meanwhile
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b in table:
+        kc2[b] = np.nan
+        vc2[b] = np.nan
+    new_table = [0, 11, 5, 3]
+    in_pairs = [(i, b) for i, b in enumerate(new_table)]
+    untouched = [b for b in range(NB) if b not in new_table]
+    snap = kc2[untouched].tobytes()
+    P.copy_blocks(kc2, host_k, in_pairs)
+    P.copy_blocks(vc2, host_v, in_pairs)
+    assert kc2[untouched].tobytes() == snap
+    after = P.paged_decode(q, kc2, vc2, np.array([new_table], np.int32), np.array([n], np.int32),
+                           B, 0.3, "f32")
+    assert after.tobytes() == before.tobytes()
