@@ -134,6 +134,65 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
                       f"{tokens} head-tokens in {el:.1f} s, float64 numpy, 1 thread on {cpu}"}
 
 
+def bench_copy_blocks(args) -> dict:
+    """Whole-block copies (pa_copy_blocks) on LLaMA-13B-shaped bf16 pools
+    (40 kv heads x 16 tokens x 128 dims = 160 KB per block and pool):
+    copy on write of --pairs random blocks inside the device pools, and a
+    swap of the same number of blocks out to pinned host memory and back.
+    Bytes = read + write of both pools."""
+    import torch
+
+    import paged_kv_cache_368_amd as pa
+
+    Hkv, B, D, npairs = 40, 16, 128, args.pairs
+    NB = max(4 * npairs, 8192)
+    block_bytes = Hkv * B * D * 2
+    g = torch.Generator().manual_seed(11)
+    kc = torch.randn((NB, Hkv, B, D), generator=g).to(torch.bfloat16).cuda()
+    vc = torch.randn((NB, Hkv, B, D), generator=g).to(torch.bfloat16).cuda()
+    perm = torch.randperm(NB, generator=g)
+    pairs = torch.stack([perm[:npairs], perm[npairs:2 * npairs]], 1).to(torch.int32).cuda()
+    host_k = torch.empty((npairs, Hkv, B, D), dtype=torch.bfloat16, pin_memory=True)
+    host_v = torch.empty_like(host_k, pin_memory=True)
+    out_pairs = torch.stack([perm[:npairs], torch.arange(npairs)], 1).to(torch.int32).cuda()
+    in_pairs = torch.stack([torch.arange(npairs), perm[2 * npairs:3 * npairs]], 1).to(torch.int32).cuda()
+    torch.cuda.synchronize()
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+        return sum(ts) / len(ts)
+
+    moved = 2 * 2 * npairs * block_bytes          # read + write, K and V
+    t_cow = timed(lambda: pa.pa_copy_blocks(kc, kc, pairs, vc, vc), args.steps)
+    t_out = timed(lambda: pa.pa_copy_blocks(host_k, kc, out_pairs, host_v, vc), max(3, args.steps // 5))
+    t_in = timed(lambda: pa.pa_copy_blocks(kc, host_k, in_pairs, vc, host_v), max(3, args.steps // 5))
+    one_way = 2 * npairs * block_bytes
+    return {
+        "metric": "block copy (pa_copy_blocks): copy-on-write GB/s in HBM, swap GB/s over the host link",
+        "value": moved / t_cow / 1e9, "unit": "GB/s (read+write)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_cow * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random bf16 pools, random block pairs)",
+        "config": {"workload": "llama13b_bf16_block_copy", "num_kv_heads": Hkv, "block_size": B,
+                   "head_dim": D, "pairs": npairs, "block_bytes": block_bytes},
+        "roofline": {"bound": "hbm", "achieved": moved / t_cow / 1e9, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": moved / t_cow / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "copy_blocks_kernel (copy on write)"},
+        "swap_out_gbps": one_way / t_out / 1e9, "swap_in_gbps": one_way / t_in / 1e9,
+        "swap_out_us": t_out * 1e6, "swap_in_us": t_in * 1e6, "cpu_baseline": None,
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +203,9 @@ def main(argv=None) -> int:
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=["decode", "copy_blocks"], default="decode",
+                    help="decode (the headline step, default) or whole-block copies")
+    ap.add_argument("--pairs", type=int, default=2048, help="block pairs for --op copy_blocks")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     args = ap.parse_args(argv)
@@ -160,6 +222,9 @@ def main(argv=None) -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pa.load_library()
+    if args.op == "copy_blocks":
+        print(json.dumps(bench_copy_blocks(args)), flush=True)
+        return 0
     dev_name = torch.cuda.get_device_name(0)
     print(f"[bench] device {dev_name}; building workload {args.config}", file=sys.stderr, flush=True)
     wl = make_workload(args.config, seed=args.seed, block_size=args.block_size)

@@ -186,14 +186,17 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
  *   dst_k, dst_v     out  pools of dst_num_blocks blocks of block_bytes each
  *   src_k, src_v     in   pools of src_num_blocks blocks of block_bytes each
  *                         (dst_v and src_v may both be NULL: one pool only)
- *   block_pairs      in   DEVICE int32 [num_pairs][2] = (src block, dst block)
+ *   block_pairs      in   int32 [num_pairs][2] = (src block, dst block), in
+ *                         device or pinned host memory
  *   block_bytes           bytes of one physical block (num_kv_heads *
  *                         block_size * head_dim * element bytes for the
  *                         layouts of pa_decode); a multiple of 16
  *
  * Every pool pointer is device memory, or pinned host memory from
  * hipHostMalloc (mapped into the device address space: the kernel then
- * reads or writes across the host link).  Pools must be 16-byte aligned.  A
+ * reads or writes across the host link); the library asks the HIP runtime
+ * for each pointer's device view and returns PA_ERR_INVALID_ARGUMENT for
+ * memory a kernel cannot reach.  Pools must be 16-byte aligned.  A
  * pair whose src or dst is outside its pool is skipped.  Pairs are copied in
  * no particular order: a block that is the dst of one pair and the src of
  * another in the same call gives an unspecified result.

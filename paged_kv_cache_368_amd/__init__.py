@@ -11,6 +11,7 @@ from ._capi import (  # noqa: F401
     declared_functions,
     load_library,
     pa_cache_write,
+    pa_copy_blocks,
     pa_compute_slots,
     pa_decode,
     pa_decode_partition_size,

@@ -55,6 +55,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, i32, i32, i32,
                               c.c_float, i32, ptr, sz, c.c_int, ptr]
     lib.pa_decode.restype = st
+    lib.pa_copy_blocks.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, c.c_int64, i32, i32, ptr]
+    lib.pa_copy_blocks.restype = st
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = c.c_char_p
     lib.pa_version.argtypes = []
@@ -171,6 +173,41 @@ def pa_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tens
         ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
         ctypes.c_void_p(slot_mapping.data_ptr()), key.shape[0], Hkv, D, B, NB,
         DTYPE_CODES[key.dtype], _stream(key)))
+
+
+def _mem(t: torch.Tensor, name: str) -> None:
+    """A pool for pa_copy_blocks: a contiguous device tensor or a pinned host one."""
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor")
+    if t.device.type != "cuda" and not t.is_pinned():
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+
+
+def pa_copy_blocks(dst_key: torch.Tensor, src_key: torch.Tensor, block_pairs: torch.Tensor,
+                   dst_value: torch.Tensor | None = None,
+                   src_value: torch.Tensor | None = None) -> None:
+    """Copy whole blocks ``dst[d] = src[s]`` for each (s, d) row of the device
+    int32 ``block_pairs`` [n][2]; pools are [num_blocks][...] device tensors
+    or pinned host tensors of one dtype.  Launches on the current stream."""
+    lib = load_library()
+    _dev(block_pairs, "block_pairs")
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int32 [n][2]")
+    pools = [("dst_key", dst_key), ("src_key", src_key)]
+    if (dst_value is None) != (src_value is None):
+        raise ValueError("give both dst_value and src_value, or neither")
+    if dst_value is not None:
+        pools += [("dst_value", dst_value), ("src_value", src_value)]
+    for n, t in pools:
+        _mem(t, n)
+    block_bytes = src_key[0].numel() * src_key.element_size() if src_key.shape[0] else 0
+    for n, t in pools:
+        if t.element_size() * (t[0].numel() if t.shape[0] else 0) != block_bytes:
+            raise ValueError(f"{n} has a different block size")
+    _check(lib.pa_copy_blocks(
+        ctypes.c_void_p(dst_key.data_ptr()), _opt(dst_value), ctypes.c_void_p(src_key.data_ptr()),
+        _opt(src_value), ctypes.c_void_p(block_pairs.data_ptr()), block_pairs.shape[0],
+        block_bytes, dst_key.shape[0], src_key.shape[0], _stream(block_pairs)))
 
 
 def pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,

@@ -29,6 +29,28 @@ int ilog2(int v) {
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
+// The address a kernel uses for a pool that is device memory or pinned host
+// memory (hipHostMalloc, mapped into the device address space).  Returns
+// nullptr for anything else (pageable host memory, unknown pointers), so no
+// kernel is ever handed an address it cannot reach.
+const void *device_view(const void *p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();                  // clear the runtime's record of the query
+    return nullptr;
+  }
+  switch (at.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+    case hipMemoryTypeUnified:
+      return p;
+    case hipMemoryTypeHost:
+      return at.devicePointer;
+    default:
+      return nullptr;
+  }
+}
+
 // The automatic partition length.  Measured on MI355X: longer partitions are
 // faster (fewer work-group prologues, no merge pass when one partition covers
 // the context), so one partition per context up to 4096 tokens, 2048-token
@@ -152,6 +174,42 @@ pa_status_t pa_cache_write(const void *key, const void *value, void *key_cache,
   hipError_t e = pa::launch_cache_write(key, value, key_cache, value_cache, slot_mapping,
                                         num_tokens, num_kv_heads, row_bytes, block_size,
                                         num_blocks, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+pa_status_t pa_copy_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
+                           const int32_t *block_pairs, int32_t num_pairs, int64_t block_bytes,
+                           int32_t dst_num_blocks, int32_t src_num_blocks, hipStream_t stream) {
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_pairs must be >= 0");
+  if (block_bytes <= 0 || block_bytes % 16 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "block_bytes must be a positive multiple of 16");
+  if (dst_num_blocks <= 0 || src_num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "dst_num_blocks and src_num_blocks must be > 0");
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_k || !src_k || !block_pairs)
+    return fail(PA_ERR_INVALID_ARGUMENT, "dst_k, src_k and block_pairs must not be NULL");
+  if (!dst_v != !src_v)
+    return fail(PA_ERR_INVALID_ARGUMENT, "dst_v and src_v must both be given or both be NULL");
+  if (!aligned16(dst_k) || !aligned16(src_k) || (dst_v && (!aligned16(dst_v) || !aligned16(src_v))))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pools must be 16-byte aligned");
+  const void *views[4] = {dst_k, dst_v, src_k, src_v};
+  for (int i = 0; i < 4; ++i) {
+    if (!views[i]) continue;
+    views[i] = device_view(views[i]);
+    if (!views[i])
+      return fail(PA_ERR_INVALID_ARGUMENT,
+                  "every pool must be device memory or pinned (hipHostMalloc) host memory");
+  }
+  const int32_t *pairs = static_cast<const int32_t *>(device_view(block_pairs));
+  if (!pairs)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "block_pairs must be device memory or pinned (hipHostMalloc) host memory");
+  hipError_t e = pa::launch_copy_blocks(const_cast<void *>(views[0]), const_cast<void *>(views[1]),
+                                        views[2], views[3], pairs, num_pairs, block_bytes,
+                                        dst_num_blocks, src_num_blocks, stream);
+  if (e == hipErrorInvalidValue)
+    return fail(PA_ERR_UNSUPPORTED, "too many pairs for one launch");
   if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
   return PA_OK;
 }

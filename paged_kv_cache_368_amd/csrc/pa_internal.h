@@ -70,6 +70,10 @@ hipError_t launch_cache_write(const void *key, const void *value, void *key_cach
                               int num_kv_heads, int row_bytes, int block_size, int num_blocks,
                               hipStream_t stream);
 
+hipError_t launch_copy_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
+                              const int32_t *pairs, int num_pairs, long long block_bytes,
+                              int dst_num_blocks, int src_num_blocks, hipStream_t stream);
+
 hipError_t launch_compute_slots(int64_t *slot_mapping, const int32_t *block_tables,
                                 int max_blocks_per_seq, const int32_t *context_lens,
                                 const int32_t *seq_ids, const int32_t *positions,

@@ -12,25 +12,14 @@ import pytest
 import torch
 
 import oracle.paged as P
+import tests._bounds as B
 import paged_kv_cache_368_amd as pa
 from workloads import build, from_torch, make_workload, to_device, to_torch
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
-MANT_BITS = {"f16": 10, "bf16": 7}
-
-
-def _bound(ref, dtype):
-    """Per-element bar: the stated tolerance, widened for 16-bit outputs to
-    one unit in the last place of the storage type at |ref| (the result has
-    to be rounded to that type; at |out| > 0.5 a bf16 half-ulp alone exceeds
-    2e-3).  At the workload shapes |out| stays well below that."""
-    tol = TOL[dtype]
-    if dtype == "f32":
-        return np.full(np.shape(ref), tol)
-    e = np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -30)))
-    return np.maximum(tol, 2.0 ** (e - MANT_BITS[dtype]))
+TOL = B.TOL
+_bound = B.bound
 
 
 def _say(msg):
@@ -59,15 +48,7 @@ def _oracle(wl, pairs=None):
                           wl.block_size, wl.scale, wl.dtype, wl.num_kv_heads, pairs=pairs)
 
 
-def _assert_close(got, ref, dtype, what):
-    assert np.isfinite(got).all(), f"{what}: non-finite output at {np.argwhere(~np.isfinite(got))[:4]}"
-    if not got.size:
-        return
-    diff = np.abs(got - ref)
-    bound = _bound(ref, dtype)
-    bad = diff > bound
-    assert not bad.any(), (f"{what}: {bad.sum()} elements over the bar; max abs err "
-                           f"{diff.max():.3e}, worst at {np.argwhere(bad)[:4].tolist()}")
+_assert_close = B.assert_close
 
 
 # ---------------------------------------------------------------------------
