@@ -100,7 +100,9 @@ def copy_blocks(dst_pool, src_pool, pairs) -> None:
 # ---------------------------------------------------------------------------
 
 def to_f64(raw: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 value of raw storage words."""
+    """Exact float64 value of raw storage words ("f64": already values)."""
+    if dtype == "f64":
+        return np.asarray(raw, dtype=np.float64)
     if dtype == "f32":
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
     if dtype == "f16":
@@ -269,6 +271,92 @@ def blockwise_softmax_sum(q, K, V, scale: float, block_size: int) -> np.ndarray:
     for b0 in range(0, n, block_size):
         total = total + attention(q, K[b0:b0 + block_size], V[b0:b0 + block_size], scale)
     return total
+
+
+
+# ---------------------------------------------------------------------------
+# 8-bit KV storage.  The pages advise storing KV in a lower precision to save
+# memory (P1 §4: blocks in bfloat16 halve memory at a small accuracy cost;
+# P1 §5 and P2 §5: quantisation and compression of the cache) without fixing
+# a format.  Reading: K and V pools hold OCP FP8 E4M3 codes (1 sign bit, 4
+# exponent bits with bias 7, 3 mantissa bits; exponent field 0 is subnormal;
+# 0x7F / 0xFF are NaN; no infinities; largest finite 448), one float32 scale
+# per pool: value = decode(code) * scale.  Writing a float x stores
+# encode(x / scale), the division done in float32 (the precision the kernel
+# works in), rounded to the nearest code with ties to the even code and
+# saturated at +-448.
+# ---------------------------------------------------------------------------
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Float64 values of E4M3 codes, from the bit fields."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    exp = (c >> 3) & 0xF
+    man = c & 0x7
+    normal = sign * (1.0 + man / 8.0) * np.exp2(exp.astype(np.float64) - 7.0)
+    sub = sign * (man / 8.0) * 2.0 ** -6
+    out = np.where(exp == 0, sub, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """E4M3 codes of float values: nearest code, ties to the code with an even
+    last bit, magnitudes above 448 saturated to 448, NaN to 0x7F."""
+    v = np.asarray(x, dtype=np.float64)
+    table = e4m3_decode(np.arange(0x7F, dtype=np.uint8))      # values of codes 0x00 .. 0x7E
+    out = np.empty(v.shape, dtype=np.uint8)
+    flat_v, flat_o = v.reshape(-1), out.reshape(-1)
+    for i, xv in enumerate(flat_v):
+        if np.isnan(xv):
+            flat_o[i] = 0x7F
+            continue
+        a = min(abs(xv), 448.0)
+        j = int(np.searchsorted(table, a))            # table[j-1] < a <= table[j]
+        if j < len(table) and table[j] == a:
+            code = j
+        else:
+            lo, hi = j - 1, j
+            dl, dh = a - table[lo], table[hi] - a
+            code = lo if dl < dh else hi if dh < dl else (lo if lo % 2 == 0 else hi)
+        flat_o[i] = code | (0x80 if (xv < 0 or (xv == 0 and np.signbit(xv))) else 0)
+    return out
+
+
+def quantize_e4m3(x_f32, scale: float) -> np.ndarray:
+    """Codes stored for float32 values ``x_f32`` with pool scale ``scale``:
+    encode(float32(x) / float32(scale))."""
+    q = np.asarray(x_f32, dtype=np.float32) / np.float32(scale)
+    return e4m3_encode(q.astype(np.float64))
+
+
+def cache_write_fp8(key_cache, value_cache, key, value, slot_mapping, block_size: int,
+                    src_dtype: str, k_scale: float, v_scale: float) -> None:
+    """The cache write of ``cache_write`` into E4M3 pools: each row is widened
+    from its storage type to float32 and quantised with its pool's scale."""
+    kq = quantize_e4m3(to_f64(key, src_dtype).astype(np.float32), k_scale)
+    vq = quantize_e4m3(to_f64(value, src_dtype).astype(np.float32), v_scale)
+    cache_write(key_cache, value_cache, kq, vq, slot_mapping, block_size)
+
+
+def paged_decode_fp8(q, key_cache, value_cache, block_tables, context_lens, block_size: int,
+                     scale: float, q_dtype: str, k_scale: float, v_scale: float,
+                     num_kv_heads: int | None = None, pairs=None) -> np.ndarray:
+    """``paged_decode`` over E4M3 pools: each (sequence, head) gathers its
+    codes through the table, takes their values decode(code) * pool scale in
+    float64, and attends."""
+    q64 = to_f64(q, q_dtype)
+    S, H, D = q64.shape
+    Hkv = key_cache.shape[1] if num_kv_heads is None else num_kv_heads
+    ks, vs = float(np.float32(k_scale)), float(np.float32(v_scale))
+    out = np.full((S, H, D), np.nan)
+    todo = pairs if pairs is not None else [(s, h) for s in range(S) for h in range(H)]
+    for s, h in todo:
+        n = int(context_lens[s])
+        g = kv_head_of(h, H, Hkv)
+        K = e4m3_decode(gather_context(key_cache, block_tables[s], n, g, block_size)) * ks
+        V = e4m3_decode(gather_context(value_cache, block_tables[s], n, g, block_size)) * vs
+        out[s, h] = attention(q64[s, h], K, V, scale)
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -108,7 +108,51 @@ def _copy_no_bounds(dst_pool, src_pool, pairs):
         dst_pool[int(d) % dst_pool.shape[0]] = src_pool[int(s) % src_pool.shape[0]]
 
 
+def _e4m3_bias8(codes):
+    return _orig["e4m3_decode"](codes) / 2.0
+
+
+def _e4m3_no_subnormals(codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    v = _orig["e4m3_decode"](c)
+    return np.where(((c >> 3) & 0xF) == 0, 0.0, v)
+
+
+def _e4m3_truncate(x):
+    v = np.asarray(x, dtype=np.float64)
+    table = _orig["e4m3_decode"](np.arange(0x7F, dtype=np.uint8))
+    out = np.empty(v.shape, np.uint8)
+    for i, xv in enumerate(v.reshape(-1)):
+        a = min(abs(xv), 448.0)
+        j = int(np.searchsorted(table, a, side="right")) - 1
+        out.reshape(-1)[i] = j | (0x80 if xv < 0 else 0)
+    return out
+
+
+def _e4m3_ties_up(x):
+    v = np.asarray(x, dtype=np.float64)
+    table = _orig["e4m3_decode"](np.arange(0x7F, dtype=np.uint8))
+    out = np.empty(v.shape, np.uint8)
+    for i, xv in enumerate(v.reshape(-1)):
+        a = min(abs(xv), 448.0)
+        j = int(np.argmin(np.abs(table - a) - 1e-12 * np.arange(len(table))))
+        out.reshape(-1)[i] = j | (0x80 if xv < 0 else 0)
+    return out
+
+
+def _quantize_times_scale(x_f32, scale):
+    return _orig["e4m3_encode"]((np.asarray(x_f32, np.float32) * np.float32(scale)).astype(np.float64))
+
+
+def _fp8_decode_no_v_scale(q, kc, vc, bt, cl, b, scale, qd, ks, vs, hkv=None, pairs=None):
+    return _orig["paged_decode_fp8"](q, kc, vc, bt, cl, b, scale, qd, ks, 1.0, hkv, pairs)
+
+
 MUTANTS = {
+    "e4m3_decode": [_e4m3_bias8, _e4m3_no_subnormals],
+    "e4m3_encode": [_e4m3_truncate, _e4m3_ties_up],
+    "quantize_e4m3": [_quantize_times_scale],
+    "paged_decode_fp8": [_fp8_decode_no_v_scale],
     "copy_blocks": [_copy_reversed, _copy_no_bounds],
     "num_required_blocks": [_floor_blocks],
     "physical_location": [_swapped_location, _off_by_one_location],

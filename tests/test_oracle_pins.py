@@ -421,3 +421,95 @@ def test_pin_copy_blocks_swap_round_trip_keeps_attention():
     after = P.paged_decode(q, kc2, vc2, np.array([new_table], np.int32), np.array([n], np.int32),
                            B, 0.3, "f32")
     assert after.tobytes() == before.tobytes()
+
+
+# --------------------------------------------------------------------------
+# 8-bit (E4M3) KV storage
+# --------------------------------------------------------------------------
+
+def test_pin_e4m3_decode_library_and_spec_values():
+    """All 256 codes against torch's float8_e4m3fn (library routine) and the
+    format's landmark values (1.0, largest finite 448, smallest normal 2^-6,
+    smallest subnormal 2^-9, negative zero, NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = P.e4m3_decode(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], lib[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(lib[~nan]))
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6
+    assert got[0x01] == 2.0 ** -9 and got[0x80] == 0.0 and np.signbit(got[0x80])
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and got[0xFE] == -448.0
+
+
+def test_pin_e4m3_encode_nearest_ties_even_saturating():
+    """Encoding is the nearest code by brute force over every finite code,
+    ties to the even code; it agrees with torch in range (random values and
+    every midpoint between neighbouring codes), saturates at +-448 beyond
+    (torch gives NaN there: the reading here saturates), and round-trips
+    every finite code."""
+    vals = P.e4m3_decode(np.arange(0x7F, dtype=np.uint8))          # 0 .. 448
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = _rng(7)
+    x = np.concatenate([rng.standard_normal(3000) * 40, mids, -mids, vals, -vals,
+                        rng.uniform(-460, 460, 2000)]).astype(np.float32).astype(np.float64)
+    enc = P.e4m3_encode(x)
+    lib = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(enc, lib)
+    finite = np.arange(256)[(np.arange(256) & 0x7F) != 0x7F].astype(np.uint8)
+    fv = P.e4m3_decode(finite)
+    for xv, c in zip(x[:600], enc[:600]):
+        d = np.abs(fv - xv)
+        best = finite[d == d.min()]
+        if len(best) > 1:                                           # a tie (or +-0)
+            best = [b for b in best if (b & 1) == 0 and np.signbit(P.e4m3_decode(b)) == np.signbit(xv)] or best
+        assert c in best
+    assert P.e4m3_encode(np.array([500.0, 1e6, -1e6, 464.0, np.nan])).tolist() == [0x7E, 0x7E, 0xFE, 0x7E, 0x7F]
+    assert np.array_equal(P.e4m3_encode(P.e4m3_decode(finite)), finite)
+
+
+def test_pin_fp8_decode_is_attention_on_dequantized_values():
+    """Decode over E4M3 pools equals the library attention routine (float64
+    SDPA) on the gathered context's values code * scale."""
+    rng = _rng(8)
+    NB, H, Hkv, B, D = 10, 4, 2, 16, 64
+    kc = P.e4m3_encode(rng.standard_normal((NB, Hkv, B, D)) * 3)
+    vc = P.e4m3_encode(rng.standard_normal((NB, Hkv, B, D)) * 3)
+    q = rng.standard_normal((1, H, D)).astype(np.float16)
+    table = np.array([[6, 2, 9, 0]], np.int32)
+    n = 57
+    got = P.paged_decode_fp8(q, kc, vc, table, np.array([n], np.int32), B, 0.125, "f16", 0.75, 1.5)
+    rows = [table[0][t // B] for t in range(n)]
+    offs = [t % B for t in range(n)]
+    Kc = torch.tensor(P.e4m3_decode(kc[rows, :, offs, :]) * 0.75)     # [n][Hkv][D]
+    Vc = torch.tensor(P.e4m3_decode(vc[rows, :, offs, :]) * 1.5)
+    G = H // Hkv
+    qt = torch.tensor(P.to_f64(q, "f16"))[0]                            # [H][D]
+    for h in range(H):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt[h][None, None], Kc[:, h // G][None], Vc[:, h // G][None], scale=0.125)[0, 0].numpy()
+        assert np.abs(got[0, h] - ref).max() < 1e-12
+
+
+def test_pin_fp8_cache_write_quantises_with_pool_scale():
+    """The fp8 cache write stores encode(float32(x) / scale) for each new row
+    in its slot and leaves other slots untouched; decode(code) * scale is
+    within half a code spacing of x."""
+    rng = _rng(9)
+    NB, Hkv, B, D = 6, 2, 4, 16
+    kc = np.full((NB, Hkv, B, D), 0x55, np.uint8)
+    vc = kc.copy()
+    key = rng.standard_normal((3, Hkv, D)).astype(np.float16)
+    val = rng.standard_normal((3, Hkv, D)).astype(np.float16)
+    slots = np.array([5, 22, -1], np.int64)
+    P.cache_write_fp8(kc, vc, key, val, slots, B, "f16", 0.01, 0.02)
+    for i, slot in enumerate(slots[:2]):
+        b, o = slot // B, slot % B
+        xk = key[i].astype(np.float64)
+        back = P.e4m3_decode(kc[b, :, o, :]) * np.float64(np.float32(0.01))
+        spacing = np.maximum(np.exp2(np.floor(np.log2(np.abs(xk / 0.01) + 1e-30)) - 3), 2.0 ** -9)
+        assert (np.abs(back - xk) <= 0.5 * spacing * 0.01 * (1 + 1e-6)).all()
+    touched = np.zeros((NB, B), bool)
+    touched[5 // B, 5 % B] = touched[22 // B, 22 % B] = True
+    assert (kc.transpose(0, 2, 1, 3)[~touched] == 0x55).all()
