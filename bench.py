@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode: context tokens/s + achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
-ELEM = {"f32": 4, "f16": 2, "bf16": 2}
+ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
 # HBM traffic of one pa_decode call, from two rocprofv3 --pmc runs of this
 # script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, summed over the
@@ -55,15 +55,17 @@ COUNTERS = {
 }
 
 
-def algorithmic_bytes(context_lens, num_heads, num_kv_heads, head_dim, block_size, dtype) -> dict:
+def algorithmic_bytes(context_lens, num_heads, num_kv_heads, head_dim, block_size, dtype,
+                      kv_dtype=None) -> dict:
     """Bytes a decode launch must move at minimum: K and V rows of every
     context token (per kv head), q and out (per query head) and the 4-byte
     table entries in use.  Per token per kv head K+V is 2*D*e bytes, the
     per-layer form of the KV size formula (2 x tokens x heads x head_dim x
     element bytes)."""
     e = ELEM[dtype]
+    ekv = ELEM[kv_dtype or dtype]
     ctx = [int(c) for c in context_lens]
-    kv = sum(ctx) * num_kv_heads * head_dim * e * 2
+    kv = sum(ctx) * num_kv_heads * head_dim * ekv * 2
     qo = 2 * len(ctx) * num_heads * head_dim * e
     table = sum(-(-c // block_size) for c in ctx) * 4
     return {"kv": kv, "q_out": qo, "table": table, "total": kv + qo + table}
@@ -108,8 +110,14 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
     try:
         t0 = time.perf_counter()
         for s, h in pairs:
-            P.paged_decode(wl.q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens,
-                           wl.block_size, wl.scale, wl.dtype, wl.num_kv_heads, pairs=[(s, h)])
+            if wl.pool_dtype == "fp8":
+                P.paged_decode_fp8(wl.q, wl.key_cache, wl.value_cache, wl.block_tables,
+                                   wl.context_lens, wl.block_size, wl.scale, wl.dtype,
+                                   wl.k_scale, wl.v_scale, wl.num_kv_heads, pairs=[(s, h)])
+            else:
+                P.paged_decode(wl.q, wl.key_cache, wl.value_cache, wl.block_tables,
+                               wl.context_lens, wl.block_size, wl.scale, wl.dtype,
+                               wl.num_kv_heads, pairs=[(s, h)])
             done += 1
             tokens += int(wl.context_lens[s])
             if time.perf_counter() - t0 > budget_s:
@@ -198,7 +206,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (default: LLaMA-7B shape)")
+    ap.add_argument("--config", type=int, default=1,
+                    help="workload index 0..5 (default 1: LLaMA-7B shape; 5: the same with fp8 K/V)")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--seed", type=int, default=None)
@@ -234,9 +243,12 @@ def main(argv=None) -> int:
     dt = wl.dtype
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
     maxctx = wl.max_context_len
-    P_used = pa.pa_decode_partition_size(S, H, Hkv, D, B, maxctx, wl.partition_size, tdt)
-    ws_bytes = pa.pa_decode_workspace_size(S, H, Hkv, D, B, maxctx, wl.partition_size, tdt)
-    nbytes = algorithmic_bytes(wl.context_lens, H, Hkv, D, B, dt)
+    fp8 = wl.pool_dtype == "fp8"
+    size_dt = pa.PA_FP8_E4M3 if fp8 else pa.DTYPE_CODES[tdt]
+    lib = pa.load_library()
+    P_used = lib.pa_decode_partition_size(S, H, Hkv, D, B, maxctx, wl.partition_size, size_dt)
+    ws_bytes = lib.pa_decode_workspace_size(S, H, Hkv, D, B, maxctx, wl.partition_size, size_dt)
+    nbytes = algorithmic_bytes(wl.context_lens, H, Hkv, D, B, dt, wl.pool_dtype)
     sum_ctx = int(wl.context_lens.sum())
 
     base = to_device(wl)
@@ -256,11 +268,20 @@ def main(argv=None) -> int:
     def step(i, ev=None):
         kc, vc = pools[i % copies]
         pa.pa_compute_slots(slots, base.block_tables, B, wl.num_blocks, context_lens=base.context_lens)
-        pa.pa_cache_write(base.new_key, base.new_value, kc, vc, slots)
+        if fp8:
+            pa.pa_cache_write_fp8(base.new_key, base.new_value, kc, vc, slots, wl.k_scale,
+                                  wl.v_scale)
+        else:
+            pa.pa_cache_write(base.new_key, base.new_value, kc, vc, slots)
         if ev is not None:
             ev[0].record(stream)
-        pa.pa_decode(base.out, base.q, kc, vc, base.block_tables, base.context_lens, maxctx,
-                     wl.scale, wl.partition_size, workspace)
+        if fp8:
+            pa.pa_decode_fp8(base.out, base.q, kc, vc, base.block_tables, base.context_lens,
+                             maxctx, wl.k_scale, wl.v_scale, wl.scale, wl.partition_size,
+                             workspace)
+        else:
+            pa.pa_decode(base.out, base.q, kc, vc, base.block_tables, base.context_lens, maxctx,
+                         wl.scale, wl.partition_size, workspace)
         if ev is not None:
             ev[1].record(stream)
 
@@ -304,7 +325,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dt,
+        "dtype": dt if not fp8 else f"{dt} (K/V fp8 e4m3)",
         "data": "synthetic (seeded N(0,1) K/V/q, random block tables; no dataset)",
         "config": {"workload": wl.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": B, "sum_context_tokens": sum_ctx,

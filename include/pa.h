@@ -46,7 +46,12 @@
 extern "C" {
 #endif
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
+/* PA_FP8_E4M3 is a K/V pool type only (pa_cache_write_fp8, pa_decode_fp8, and
+ * the dtype argument of the sizing functions for those pools): OCP FP8 E4M3
+ * codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7F and 0xFF
+ * are NaN; largest finite 448), one float32 scale per pool, value = code *
+ * scale. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype_t;
 
 typedef enum {
   PA_OK = 0,
@@ -172,6 +177,46 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
                       int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                       int32_t partition_size, void *workspace, size_t workspace_bytes,
                       pa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * pa_cache_write_fp8 -- pa_cache_write into E4M3 pools.  The pages advise
+ * keeping the cache in a lower precision to save memory (P1 §4 keeps blocks
+ * in bfloat16; P1 §5 and P2 §5 quantise and compress the cache); this build's
+ * reading is 8-bit E4M3 codes with one float32 scale per pool.  Each element
+ * x of a new row (storage type src_dtype, widened exactly to float32) is
+ * stored as the E4M3 code nearest to x / scale (IEEE float32 division), ties
+ * to the even code, magnitudes above 448 saturated to 448, NaN as 0x7F:
+ *   key_cache[slot / B][h][slot % B][d] = code(key[i][h][d] / k_scale)
+ * (the same for value with v_scale).  Bit-exact by definition.
+ *
+ *   key, value             in     [num_tokens][num_kv_heads][head_dim], src_dtype
+ *   key_cache, value_cache in/out uint8 [num_blocks][num_kv_heads][block_size][head_dim]
+ *   slot_mapping           in     int64 [num_tokens]; out-of-range slots are skipped
+ *   k_scale, v_scale             finite and > 0
+ * Supported: head_dim a multiple of 16; src_dtype PA_F32, PA_F16 or PA_BF16.
+ */
+pa_status_t pa_cache_write_fp8(const void *key, const void *value, void *key_cache,
+                               void *value_cache, const int64_t *slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks, pa_dtype_t src_dtype,
+                               float k_scale, float v_scale, hipStream_t stream);
+
+/*
+ * pa_decode_fp8 -- pa_decode over E4M3 pools: attention over the stored
+ * values code * k_scale (keys) and code * v_scale (values); q and out are
+ * fp16 or bf16 (q_dtype), arithmetic is float32.  Every other argument,
+ * the partition and workspace rules (size them with dtype PA_FP8_E4M3) and
+ * the handling of invalid device values are those of pa_decode.  Runs on the
+ * vector units for every head grouping.
+ */
+pa_status_t pa_decode_fp8(void *out, const void *q, const void *key_cache,
+                          const void *value_cache, const int32_t *block_tables,
+                          const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t max_context_len, float scale, float k_scale, float v_scale,
+                          int32_t partition_size, void *workspace, size_t workspace_bytes,
+                          pa_dtype_t q_dtype, hipStream_t stream);
 
 /*
  * pa_copy_blocks -- copy whole physical blocks from one pair of pools to

@@ -10,10 +10,13 @@ from ._capi import (  # noqa: F401
     PaError,
     declared_functions,
     load_library,
+    PA_FP8_E4M3,
     pa_cache_write,
+    pa_cache_write_fp8,
     pa_copy_blocks,
     pa_compute_slots,
     pa_decode,
+    pa_decode_fp8,
     pa_decode_partition_size,
     pa_decode_workspace_size,
     pa_last_error,

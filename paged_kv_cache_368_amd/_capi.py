@@ -55,6 +55,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, i32, i32, i32,
                               c.c_float, i32, ptr, sz, c.c_int, ptr]
     lib.pa_decode.restype = st
+    f32 = c.c_float
+    lib.pa_cache_write_fp8.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, c.c_int,
+                                       f32, f32, ptr]
+    lib.pa_cache_write_fp8.restype = st
+    lib.pa_decode_fp8.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, i32, i32,
+                                  i32, f32, f32, f32, i32, ptr, sz, c.c_int, ptr]
+    lib.pa_decode_fp8.restype = st
     lib.pa_copy_blocks.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, c.c_int64, i32, i32, ptr]
     lib.pa_copy_blocks.restype = st
     lib.pa_last_error.argtypes = []
@@ -208,6 +215,75 @@ def pa_copy_blocks(dst_key: torch.Tensor, src_key: torch.Tensor, block_pairs: to
         ctypes.c_void_p(dst_key.data_ptr()), _opt(dst_value), ctypes.c_void_p(src_key.data_ptr()),
         _opt(src_value), ctypes.c_void_p(block_pairs.data_ptr()), block_pairs.shape[0],
         block_bytes, dst_key.shape[0], src_key.shape[0], _stream(block_pairs)))
+
+
+PA_FP8_E4M3 = 3
+
+
+def pa_cache_write_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float,
+                       v_scale: float) -> None:
+    """Quantise key/value [T][Hkv][D] (f32/f16/bf16) into uint8 E4M3 pools
+    [NB][Hkv][B][D] at their slots: code(x / scale)."""
+    lib = load_library()
+    for n, t in (("key", key), ("value", value), ("key_cache", key_cache),
+                 ("value_cache", value_cache), ("slot_mapping", slot_mapping)):
+        _dev(t, n)
+    if key.dtype not in DTYPE_CODES or value.dtype != key.dtype:
+        raise ValueError("key and value must share one of float32/float16/bfloat16")
+    if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8:
+        raise ValueError("E4M3 pools are uint8 tensors")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != key.shape[0]:
+        raise ValueError("slot_mapping must be int64 with one entry per token")
+    NB, Hkv, B, D = key_cache.shape
+    if tuple(value_cache.shape) != (NB, Hkv, B, D) or key.shape[1:] != (Hkv, D) or value.shape != key.shape:
+        raise ValueError("shape mismatch between key/value and the pools")
+    _check(lib.pa_cache_write_fp8(
+        ctypes.c_void_p(key.data_ptr()), ctypes.c_void_p(value.data_ptr()),
+        ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
+        ctypes.c_void_p(slot_mapping.data_ptr()), key.shape[0], Hkv, D, B, NB,
+        DTYPE_CODES[key.dtype], float(k_scale), float(v_scale), _stream(key)))
+
+
+def pa_decode_fp8(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                  value_cache: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, max_context_len: int, k_scale: float,
+                  v_scale: float, scale: float | None = None, partition_size: int = 0,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """PagedAttention decode over uint8 E4M3 pools (values code * scale) into
+    ``out`` [S][H][D] of q's type (fp16/bf16); see include/pa.h."""
+    lib = load_library()
+    for n, t in (("out", out), ("q", q), ("key_cache", key_cache), ("value_cache", value_cache),
+                 ("block_tables", block_tables), ("context_lens", context_lens)):
+        _dev(t, n)
+    if q.dtype not in (torch.float16, torch.bfloat16) or out.dtype != q.dtype:
+        raise ValueError("q and out must share float16 or bfloat16")
+    if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8:
+        raise ValueError("E4M3 pools are uint8 tensors")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    S, H, D = q.shape
+    NB, Hkv, B, D2 = key_cache.shape
+    if D2 != D or tuple(value_cache.shape) != (NB, Hkv, B, D) or tuple(out.shape) != (S, H, D):
+        raise ValueError("shape mismatch between q, out and the pools")
+    if block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables and context_lens must have one row per sequence")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    n = lib.pa_decode_workspace_size(S, H, Hkv, D, B, max_context_len, partition_size, PA_FP8_E4M3)
+    if n == ctypes.c_size_t(-1).value:
+        raise PaError(PA_ERR_INVALID_ARGUMENT, pa_last_error())
+    if n and workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode_fp8(
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(context_lens.data_ptr()),
+        S, H, Hkv, D, B, NB, block_tables.shape[1], max_context_len, float(scale), float(k_scale),
+        float(v_scale), partition_size, ws_ptr, ws_bytes, DTYPE_CODES[q.dtype], _stream(q)))
+    return out
 
 
 def pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,

@@ -58,7 +58,121 @@ __global__ __launch_bounds__(256) void compute_slots_kernel(
   slot_mapping[i] = slot;
 }
 
+// E4M3 code of a float32 value (the value already divided by the pool's
+// scale): nearest code with ties to the even code, magnitudes above 448
+// saturated to 448, NaN to 0x7F.  Done by exact power-of-two scaling and
+// rintf (round to nearest even on the integer grid of the target format), so
+// no hardware conversion mode is involved.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t bits = __builtin_bit_cast(uint32_t, x);
+  if ((bits & 0x7fffffffu) > 0x7f800000u) return 0x7fu;
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fminf(__builtin_fabsf(x), 448.f);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = (uint32_t)__builtin_rintf(a * 512.f);             // subnormal grid, step 2^-9
+  } else {
+    const uint32_t ab = __builtin_bit_cast(uint32_t, a);
+    const int e = (int)(ab >> 23) - 127;                      // 2^e <= a < 2^(e+1), e in [-6, 8]
+    const float m = __builtin_bit_cast(float, (ab & 0x007fffffu) | 0x3f800000u);   // a / 2^e
+    const uint32_t mq = (uint32_t)__builtin_rintf((m - 1.f) * 8.f);   // 0..8; 8 carries
+    code = ((uint32_t)(e + 7) << 3) + mq;
+  }
+  return code | sign;
+}
+
+// Cache write into E4M3 pools: one thread converts 16 elements of a K row
+// (and of the matching V row) and stores their 16 codes with one 16-byte
+// store.  ST: the source rows' storage type.
+template <int ST>
+__global__ __launch_bounds__(256) void cache_write_fp8_kernel(
+    const char *__restrict__ key, const char *__restrict__ value, uint8_t *__restrict__ key_cache,
+    uint8_t *__restrict__ value_cache, const int64_t *__restrict__ slot_mapping, int num_tokens,
+    int num_kv_heads, int head_dim, int block_size, long long pool_slots, float k_scale,
+    float v_scale) {
+  constexpr int ES = Storage<ST>::kBytes;
+  constexpr int SW = 16 * ES / 16;                          // 16-byte source words per piece
+  const int pieces = head_dim / 16;
+  const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long per_token = (long long)num_kv_heads * pieces;
+  if (u >= per_token * num_tokens) return;
+  const int i = (int)(u / per_token);
+  const int rem = (int)(u - (long long)i * per_token);
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= pool_slots) return;
+  const long long blk = slot / block_size;
+  const int off = (int)(slot - blk * block_size);
+  const int h = rem / pieces;
+  const int c = rem - h * pieces;
+  const long long src = (((long long)i * num_kv_heads + h) * head_dim + c * 16) * ES;
+  const long long dst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + c * 16;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const char *in = (which == 0 ? key : value) + src;
+    const float scale = which == 0 ? k_scale : v_scale;
+    u32x4 w[SW];
+#pragma unroll
+    for (int j = 0; j < SW; ++j) w[j] = reinterpret_cast<const u32x4 *>(in)[j];
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < SW; ++j) {
+      const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (ST == kF32) {
+          x[4 * j + k] = as_f32(ww[k]);
+        } else {
+          x[8 * j + 2 * k] = lo_f32<ST>(ww[k]);
+          x[8 * j + 2 * k + 1] = hi_f32<ST>(ww[k]);
+        }
+      }
+    }
+    uint32_t out[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) word |= e4m3_code(x[4 * k + b] / scale) << (8 * b);
+      out[k] = word;
+    }
+    *reinterpret_cast<u32x4 *>((which == 0 ? key_cache : value_cache) + dst) =
+        u32x4{out[0], out[1], out[2], out[3]};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cache_write_fp8(const void *key, const void *value, void *key_cache,
+                                  void *value_cache, const int64_t *slot_mapping, int num_tokens,
+                                  int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                  int src_dt, float k_scale, float v_scale, hipStream_t stream) {
+  const long long total = (long long)num_tokens * num_kv_heads * (head_dim / 16);
+  if (total <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  const long long slots = (long long)num_blocks * block_size;
+  const char *k = static_cast<const char *>(key), *v = static_cast<const char *>(value);
+  uint8_t *kc = static_cast<uint8_t *>(key_cache), *vc = static_cast<uint8_t *>(value_cache);
+  switch (src_dt) {
+    case kF32:
+      hipLaunchKernelGGL(cache_write_fp8_kernel<kF32>, dim3(grid), dim3(256), 0, stream, k, v, kc,
+                         vc, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, slots,
+                         k_scale, v_scale);
+      break;
+    case kF16:
+      hipLaunchKernelGGL(cache_write_fp8_kernel<kF16>, dim3(grid), dim3(256), 0, stream, k, v, kc,
+                         vc, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, slots,
+                         k_scale, v_scale);
+      break;
+    case kBF16:
+      hipLaunchKernelGGL(cache_write_fp8_kernel<kBF16>, dim3(grid), dim3(256), 0, stream, k, v,
+                         kc, vc, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size,
+                         slots, k_scale, v_scale);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_cache_write(const void *key, const void *value, void *key_cache,
                               void *value_cache, const int64_t *slot_mapping, int num_tokens,

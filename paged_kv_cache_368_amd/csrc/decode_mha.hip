@@ -39,56 +39,93 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
-template <int DT, int D>
+template <int KT, int D>
 struct MhaShape {
-  static constexpr int kE = Storage<DT>::kBytes;
+  static constexpr int kE = Storage<KT>::kBytes;  // bytes per K/V element
   static constexpr int kEpl = 16 / kE;          // elements per lane per load
   static constexpr int kLpt = D / kEpl;         // lanes per token row
   static constexpr int kTpl = 64 / kLpt;        // token rows per wave load
   static constexpr int kLoads = kChunk / kTpl;  // loads per chunk, K and V each
-  static_assert(kLpt == 8 || kLpt == 16 || kLpt == 32, "row width");
+  static_assert(kLpt == 4 || kLpt == 8 || kLpt == 16 || kLpt == 32, "row width");
 };
 
-// Per-lane dot of the lane's 16 bytes of q and of a K row.
-template <int DT>
-__device__ __forceinline__ float lane_dot(const u32x4 &q, const u32x4 &k) {
-  if constexpr (DT == kF32) {
-    float acc = as_f32(q.x) * as_f32(k.x);
-    acc = __builtin_fmaf(as_f32(q.y), as_f32(k.y), acc);
-    acc = __builtin_fmaf(as_f32(q.z), as_f32(k.z), acc);
-    acc = __builtin_fmaf(as_f32(q.w), as_f32(k.w), acc);
+// Two E4M3 codes (bytes 0-1 or 2-3 of a word) as a packed 16-bit pair of the
+// query's type; exact (every E4M3 value is a binary16 and a bfloat16 value).
+template <int QT, bool HI>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w) {
+  if constexpr (QT == kBF16)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// Per-lane dot of the lane's slice of q and of a K row: 16 bytes of K, and
+// q in its own type (16 bytes, or 32 bytes against 16 E4M3 codes).
+template <int QT, int KT>
+__device__ __forceinline__ float lane_dot(const u32x4 *q, const u32x4 &k) {
+  if constexpr (KT == kF32) {
+    float acc = as_f32(q[0].x) * as_f32(k.x);
+    acc = __builtin_fmaf(as_f32(q[0].y), as_f32(k.y), acc);
+    acc = __builtin_fmaf(as_f32(q[0].z), as_f32(k.z), acc);
+    acc = __builtin_fmaf(as_f32(q[0].w), as_f32(k.w), acc);
+    return acc;
+  } else if constexpr (KT == kFP8) {
+    const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+    const uint32_t qw[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = dot2<QT>(qw[2 * i], fp8_pair<QT, false>(kw[i]), acc);
+      acc = dot2<QT>(qw[2 * i + 1], fp8_pair<QT, true>(kw[i]), acc);
+    }
     return acc;
   } else {
-    float acc = dot2<DT>(q.x, k.x, 0.f);
-    acc = dot2<DT>(q.y, k.y, acc);
-    acc = dot2<DT>(q.z, k.z, acc);
-    acc = dot2<DT>(q.w, k.w, acc);
+    float acc = dot2<KT>(q[0].x, k.x, 0.f);
+    acc = dot2<KT>(q[0].y, k.y, acc);
+    acc = dot2<KT>(q[0].z, k.z, acc);
+    acc = dot2<KT>(q[0].w, k.w, acc);
     return acc;
   }
 }
 
 // o[0..EPL) += p * (the lane's 16 bytes of a V row)
-template <int DT>
+template <int KT>
 __device__ __forceinline__ void lane_axpy(float *o, float p, const u32x4 &v) {
-  if constexpr (DT == kF32) {
+  if constexpr (KT == kF32) {
     o[0] = __builtin_fmaf(p, as_f32(v.x), o[0]);
     o[1] = __builtin_fmaf(p, as_f32(v.y), o[1]);
     o[2] = __builtin_fmaf(p, as_f32(v.z), o[2]);
     o[3] = __builtin_fmaf(p, as_f32(v.w), o[3]);
+  } else if constexpr (KT == kFP8) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);   // bytes 0, 1
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);    // bytes 2, 3
+      const float f0 = lo[0], f1 = lo[1], f2 = hi[0], f3 = hi[1];
+      o[4 * i] = __builtin_fmaf(p, f0, o[4 * i]);
+      o[4 * i + 1] = __builtin_fmaf(p, f1, o[4 * i + 1]);
+      o[4 * i + 2] = __builtin_fmaf(p, f2, o[4 * i + 2]);
+      o[4 * i + 3] = __builtin_fmaf(p, f3, o[4 * i + 3]);
+    }
   } else {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      o[2 * i] = __builtin_fmaf(p, lo_f32<DT>(w[i]), o[2 * i]);
-      o[2 * i + 1] = __builtin_fmaf(p, hi_f32<DT>(w[i]), o[2 * i + 1]);
+      o[2 * i] = __builtin_fmaf(p, lo_f32<KT>(w[i]), o[2 * i]);
+      o[2 * i + 1] = __builtin_fmaf(p, hi_f32<KT>(w[i]), o[2 * i + 1]);
     }
   }
 }
 
-template <int DT, int D, int NW>
+// DT: type of q and out; KT: storage type of the K/V pools (DT, or kFP8 with
+// DT fp16/bf16).
+template <int DT, int KT, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
-  using Sh = MhaShape<DT, D>;
+  using Sh = MhaShape<KT, D>;
   constexpr int E = Sh::kE, EPL = Sh::kEpl, LPT = Sh::kLpt, TPL = Sh::kTpl, NL = Sh::kLoads;
+  constexpr int EQ = Storage<DT>::kBytes;         // bytes per q / out element
+  constexpr int QW = EPL * EQ / 16;               // 16-byte words of q per lane
   static_assert(NW * 64 >= kMaxPartBlocks, "one thread per staged block id");
 
   __shared__ int s_tbl[kMaxPartBlocks];
@@ -125,8 +162,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks_per_seq + b0;
   const int window = min(P >> a.log2_block, a.max_blocks_per_seq - b0);
   const int id = tid < window ? trow[tid] : -1;
-  const u32x4 qv = *reinterpret_cast<const u32x4 *>(
-      reinterpret_cast<const char *>(a.q) + (row_out + col * EPL) * E);
+  u32x4 qv[QW];
+#pragma unroll
+  for (int i = 0; i < QW; ++i)
+    qv[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.q) +
+                                             (row_out + col * EPL) * EQ + 16 * i);
 
   const bool bad_ctx = ctx < 0 || ctx > a.max_context_len ||
                        ctx > a.max_blocks_per_seq * a.block_size;
@@ -210,7 +250,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
     const int tc = t0 + (wave + NW * k) * kChunk;
     float sc[NL];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) sc[j] = group_sum<LPT>(lane_dot<DT>(qv, kb[j])) * a.scale_log2;
+    for (int j = 0; j < NL; ++j) sc[j] = group_sum<LPT>(lane_dot<DT, KT>(qv, kb[j])) * a.scale_log2;
     const bool tail = tc + kChunk > t1;                       // last chunk: mask past the context
     bool valid[NL];
 #pragma unroll
@@ -232,7 +272,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
       const float pj = exp2_fast(sc[j] - msafe);
       psum += pj;
       const u32x4 v = valid[j] ? vb[j] : u32x4{0u, 0u, 0u, 0u};
-      lane_axpy<DT>(o, pj, v);
+      lane_axpy<KT>(o, pj, v);
     }
     l = l * corr + psum;
     m = mnew;
@@ -298,6 +338,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
       L += f * s_l[w];
       O += f * s_o[w][tid];
     }
+    if constexpr (KT == kFP8) O *= a.v_scale;   // values are code * V pool scale
     if (direct) {
       const float r = L == 0.f ? 0.f : O / L;   // NaN (a poisoned partition) propagates
       store_out<DT>(a.out, row_out + tid, &r, 1);
@@ -398,13 +439,24 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(DecodeArgs a) {
   }
 }
 
-template <int DT, int D>
-hipError_t launch_mha_t(const DecodeArgs &a, hipStream_t stream) {
+template <int DT, int KT, int D>
+hipError_t launch_mha_kt(const DecodeArgs &a, hipStream_t stream) {
   const long n = (long)a.num_seqs * a.num_heads * a.num_partitions;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_mha_kernel<DT, D, kDecodeWaves>), dim3((unsigned)n),
+  hipLaunchKernelGGL((decode_mha_kernel<DT, KT, D, kDecodeWaves>), dim3((unsigned)n),
                      dim3(kDecodeWaves * 64), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_mha_t(const DecodeArgs &a, hipStream_t stream) {
+  return launch_mha_kt<DT, DT, D>(a, stream);
+}
+
+template <int DT, int D>
+hipError_t launch_mha_fp8_t(const DecodeArgs &a, hipStream_t stream) {
+  if constexpr (DT == kF32) return hipErrorInvalidValue;
+  else return launch_mha_kt<DT, kFP8, D>(a, stream);
 }
 
 template <int DT, int D>
@@ -428,7 +480,11 @@ hipError_t launch_merge_t(const DecodeArgs &a, hipStream_t stream) {
     default: return hipErrorInvalidValue;                                  \
   }
 
-hipError_t launch_decode_mha(const DecodeArgs &a, int dt, hipStream_t stream) {
+hipError_t launch_decode_mha(const DecodeArgs &a, int dt, int kv_dt, hipStream_t stream) {
+  if (kv_dt == kFP8) {
+    PA_DISPATCH(launch_mha_fp8_t, dt, a.head_dim, a, stream)
+  }
+  if (kv_dt != dt) return hipErrorInvalidValue;
   PA_DISPATCH(launch_mha_t, dt, a.head_dim, a, stream)
 }
 

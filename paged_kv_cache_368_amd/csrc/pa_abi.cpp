@@ -74,8 +74,8 @@ pa_status_t check_shape(int32_t num_seqs, int32_t num_heads, int32_t num_kv_head
   if (num_heads % num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_heads must be a multiple of num_kv_heads");
   if (max_context_len < 0) return fail(PA_ERR_INVALID_ARGUMENT, "max_context_len must be >= 0");
-  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "dtype must be PA_F32, PA_F16 or PA_BF16");
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16 && dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "dtype must be PA_F32, PA_F16, PA_BF16 or PA_FP8_E4M3");
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (block_size != 16 && block_size != 32 && block_size != 64)
@@ -236,16 +236,23 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
   return z.ws_bytes;
 }
 
-pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const void *value_cache,
-                      const int32_t *block_tables, const int32_t *context_lens,
-                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                      int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
-                      int32_t partition_size, void *workspace, size_t workspace_bytes,
-                      pa_dtype_t dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode and pa_decode_fp8: q/out of type q_dt, pools of type kv_dt
+// (q_dt, or PA_FP8_E4M3 with its two pool scales).
+pa_status_t decode_impl(void *out, const void *q, const void *key_cache, const void *value_cache,
+                        const int32_t *block_tables, const int32_t *context_lens,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                        int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                        float k_scale, float v_scale, int32_t partition_size, void *workspace,
+                        size_t workspace_bytes, pa_dtype_t q_dt, pa_dtype_t kv_dt,
+                        hipStream_t stream) {
   Sizes z;
   pa_status_t st = plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                        max_context_len, partition_size, dtype, &z);
+                        max_context_len, partition_size, kv_dt, &z);
   if (st != PA_OK) return st;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks and max_blocks_per_seq must be > 0");
@@ -253,6 +260,8 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
     return fail(PA_ERR_INVALID_ARGUMENT,
                 "max_context_len exceeds max_blocks_per_seq * block_size");
   if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (!isfinite(k_scale) || !isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return fail(PA_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be finite and > 0");
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARGUMENT, "pointer arguments must not be NULL");
@@ -286,14 +295,76 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale * 1.4426950408889634f * k_scale;
+  a.v_scale = v_scale;
   a.partition_size = z.partition;
   a.num_partitions = z.num_partitions;
 
-  hipError_t e = pa::gqa_supported(dtype, head_dim, num_heads, num_kv_heads)
-                     ? pa::launch_decode_gqa(a, dtype, stream)
-                     : pa::launch_decode_mha(a, dtype, stream);
-  if (e == hipSuccess && z.num_partitions > 1) e = pa::launch_merge(a, dtype, stream);
+  hipError_t e = kv_dt == q_dt && pa::gqa_supported(q_dt, head_dim, num_heads, num_kv_heads)
+                     ? pa::launch_decode_gqa(a, q_dt, stream)
+                     : pa::launch_decode_mha(a, q_dt, kv_dt, stream);
+  if (e == hipSuccess && z.num_partitions > 1) e = pa::launch_merge(a, q_dt, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      pa_dtype_t dtype, hipStream_t stream) {
+  if (dtype == PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "E4M3 pools are decoded by pa_decode_fp8");
+  return decode_impl(out, q, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, 1.f, 1.f, partition_size,
+                     workspace, workspace_bytes, dtype, dtype, stream);
+}
+
+pa_status_t pa_decode_fp8(void *out, const void *q, const void *key_cache,
+                          const void *value_cache, const int32_t *block_tables,
+                          const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t max_context_len, float scale, float k_scale, float v_scale,
+                          int32_t partition_size, void *workspace, size_t workspace_bytes,
+                          pa_dtype_t q_dtype, hipStream_t stream) {
+  if (q_dtype != PA_F16 && q_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_fp8 takes fp16 or bf16 queries");
+  return decode_impl(out, q, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, q_dtype, PA_FP8_E4M3, stream);
+}
+
+pa_status_t pa_cache_write_fp8(const void *key, const void *value, void *key_cache,
+                               void *value_cache, const int64_t *slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks, pa_dtype_t src_dtype,
+                               float k_scale, float v_scale, hipStream_t stream) {
+  if (src_dtype != PA_F32 && src_dtype != PA_F16 && src_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "src_dtype must be PA_F32, PA_F16 or PA_BF16");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0");
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "num_kv_heads, head_dim, block_size and num_blocks must be > 0");
+  if (head_dim % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 16");
+  if (!isfinite(k_scale) || !isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return fail(PA_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be finite and > 0");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pointer arguments must not be NULL");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "key, value and the pools must be 16-byte aligned");
+  hipError_t e = pa::launch_cache_write_fp8(key, value, key_cache, value_cache, slot_mapping,
+                                            num_tokens, num_kv_heads, head_dim, block_size,
+                                            num_blocks, src_dtype, k_scale, v_scale, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
   return PA_OK;
 }

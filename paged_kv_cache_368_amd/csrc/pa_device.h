@@ -26,6 +26,7 @@ template <int DT> struct Storage;
 template <> struct Storage<kF32> { static constexpr int kBytes = 4; };
 template <> struct Storage<kF16> { static constexpr int kBytes = 2; };
 template <> struct Storage<kBF16> { static constexpr int kBytes = 2; };
+template <> struct Storage<kFP8> { static constexpr int kBytes = 1; };
 
 // Widen the two 16-bit values packed in a 32-bit word.
 template <int DT> __device__ __forceinline__ float lo_f32(uint32_t w);
@@ -94,13 +95,13 @@ template <int CTRL> __device__ __forceinline__ float dpp(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over each aligned group of N lanes (N in {8, 16, 32}); every lane of the
-// group receives the total.
+// Sum over each aligned group of N lanes (N in {4, 8, 16, 32}); every lane of
+// the group receives the total.
 template <int N> __device__ __forceinline__ float group_sum(float v) {
-  static_assert(N == 8 || N == 16 || N == 32, "group");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group");
   if constexpr (N == 8) {
     v += dpp<kDppRowHalfMirror>(v);
-  } else {
+  } else if constexpr (N >= 16) {
     v += dpp<kDppRowRor8>(v);
     v += dpp<kDppRowRor4>(v);
   }

@@ -14,9 +14,10 @@ namespace pa {
 // return `st`.  Defined in pa_abi.cpp.
 pa_status_t set_error(pa_status_t st, const char *msg);
 
-enum Dt : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+// Storage types; kFP8 (OCP E4M3 codes with a per-pool scale) is a KV-pool type only.
+enum Dt : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
 
-inline int elem_bytes(int dt) { return dt == kF32 ? 4 : 2; }
+inline int elem_bytes(int dt) { return dt == kF32 ? 4 : dt == kFP8 ? 1 : 2; }
 
 // Longest partition one work-group handles: 256 chunks of 16 tokens.  Bounded
 // by the per-wave block-id register (64 lanes x 4 waves) and by the LDS copy
@@ -51,12 +52,14 @@ struct DecodeArgs {
   const int32_t *context_lens;  // [S]
   int num_seqs, num_heads, num_kv_heads, head_dim;
   int block_size, log2_block, num_blocks, max_blocks_per_seq, max_context_len;
-  float scale_log2;          // scale * log2(e): scores live in base-2 units
+  float scale_log2;          // scale * log2(e) (* the K pool scale for fp8 pools): base-2 scores
+  float v_scale;             // the V pool scale for fp8 pools (1 otherwise)
   int partition_size;        // P
   int num_partitions;        // NP = ceil(max_context_len / P), >= 1
 };
 
-hipError_t launch_decode_mha(const DecodeArgs &a, int dt, hipStream_t stream);
+// kv_dt: the pools' storage type, equal to dt or kFP8 (dt fp16/bf16 only).
+hipError_t launch_decode_mha(const DecodeArgs &a, int dt, int kv_dt, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs &a, int dt, hipStream_t stream);
 
 // Grouped-query decode on the matrix cores: fp16/bf16, head_dim 64 or 128,
@@ -73,6 +76,13 @@ hipError_t launch_cache_write(const void *key, const void *value, void *key_cach
 hipError_t launch_copy_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
                               const int32_t *pairs, int num_pairs, long long block_bytes,
                               int dst_num_blocks, int src_num_blocks, hipStream_t stream);
+
+// Cache write into E4M3 pools: rows of src_dt widened to float32, divided by
+// the pool's scale and rounded to the nearest code (ties to even), saturated.
+hipError_t launch_cache_write_fp8(const void *key, const void *value, void *key_cache,
+                                  void *value_cache, const int64_t *slot_mapping, int num_tokens,
+                                  int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                  int src_dt, float k_scale, float v_scale, hipStream_t stream);
 
 hipError_t launch_compute_slots(int64_t *slot_mapping, const int32_t *block_tables,
                                 int max_blocks_per_seq, const int32_t *context_lens,

@@ -1,0 +1,144 @@
+"""GPU parity of the 8-bit (E4M3) KV path: pa_cache_write_fp8 bit-exact
+against the oracle's quantiser, pa_decode_fp8 within the decode tolerance of
+the oracle's float64 attention over the stored values (code * pool scale)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.paged as P
+import tests._bounds as BD
+import paged_kv_cache_368_amd as pa
+from workloads import build, e4m3_codes, from_torch, make_workload, normal_array, to_device, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load_library()
+
+
+def _fp8_decode(wl, dev=None, partition_size=0):
+    dev = dev or to_device(wl)
+    pa.pa_decode_fp8(dev.out, dev.q, dev.key_cache, dev.value_cache, dev.block_tables,
+                     dev.context_lens, wl.max_context_len, wl.k_scale, wl.v_scale, wl.scale,
+                     partition_size)
+    torch.cuda.synchronize()
+    return P.to_f64(from_torch(dev.out, wl.dtype), wl.dtype)
+
+
+def _oracle(wl, pairs=None):
+    return P.paged_decode_fp8(wl.q, wl.key_cache, wl.value_cache, wl.block_tables,
+                              wl.context_lens, wl.block_size, wl.scale, wl.dtype, wl.k_scale,
+                              wl.v_scale, wl.num_kv_heads, pairs)
+
+
+@pytest.mark.parametrize("src", ["f16", "bf16", "f32"])
+def test_cache_write_fp8_bitexact(src):
+    _say(f"cache_write_fp8 from {src}")
+    NB, Hkv, B, D, T = 12, 4, 16, 128, 37
+    rng = np.random.default_rng(5)
+    key = normal_array(21, 1, (T, Hkv, D), src, 3.0)
+    value = normal_array(21, 2, (T, Hkv, D), src, 0.05)
+    # special values in the first rows: ties, saturation, zeros, tiny, NaN
+    vals = P.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2)[:D]
+    specials = np.concatenate([mids, [500.0, -1e4, 0.0, -0.0, 1e-9, -1e-9, 448.0, 464.0]])
+    sp = np.zeros(Hkv * D)
+    sp[:len(specials)] = specials
+    if src == "f32":
+        key[0] = sp.reshape(Hkv, D).astype(np.float32) * np.float32(0.5)
+        key[1, 0, 0] = np.float32(np.nan)
+    kc = np.full((NB, Hkv, B, D), 0x55, np.uint8)
+    vc = kc.copy()
+    slots = rng.choice(NB * B, T, replace=False).astype(np.int64)
+    slots[3] = -1
+    slots[4] = NB * B + 5
+    ref_k, ref_v = kc.copy(), vc.copy()
+    P.cache_write_fp8(ref_k, ref_v, key, value, slots, B, src, 0.5, 0.01)
+    dk, dv = to_torch(kc, "fp8", "cuda"), to_torch(vc, "fp8", "cuda")
+    pa.pa_cache_write_fp8(to_torch(key, src, "cuda"), to_torch(value, src, "cuda"), dk, dv,
+                          torch.tensor(slots, device="cuda"), 0.5, 0.01)
+    torch.cuda.synchronize()
+    got_k, got_v = from_torch(dk, "fp8"), from_torch(dv, "fp8")
+    bad = np.argwhere(got_k != ref_k)
+    assert not bad.size, f"{len(bad)} key codes differ, first at {bad[:3].tolist()}: " \
+        f"{got_k[tuple(bad[0])]:#x} vs {ref_k[tuple(bad[0])]:#x}"
+    assert np.array_equal(got_v, ref_v)
+
+
+@pytest.mark.parametrize("qt", ["f16", "bf16"])
+def test_context_one_returns_every_code_exactly(qt):
+    """One token whose V rows hold every finite E4M3 code: the output is
+    exactly code * v_scale (a power of two keeps it exact in the output
+    type)."""
+    _say(f"fp8 ctx=1 all codes {qt}")
+    Hkv, H, B, D = 2, 2, 16, 128
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # 254 codes
+    row = np.concatenate([finite, finite[:2 * D - len(finite)]]).reshape(Hkv, D)
+    kc = e4m3_codes(3, 1, (4, Hkv, B, D))
+    vc = e4m3_codes(3, 2, (4, Hkv, B, D))
+    vc[2, :, 0, :] = row
+    q = normal_array(3, 3, (1, H, D), qt)
+    wl = build("fp8_ctx1", qt, [1], H, Hkv, D, B, seed=3, num_blocks=4, kv_dtype="fp8",
+               kv_scale=0.25)
+    wl.key_cache, wl.value_cache, wl.q = kc, vc, q
+    wl.block_tables[:] = 2
+    got = _fp8_decode(wl)
+    want = P.e4m3_decode(row) * 0.25
+    assert np.array_equal(got[0], want), np.argwhere(got[0] != want)[:4]
+
+
+FP8_CASES = [
+    ("mha_d128", dict(ctx=[1, 15, 16, 17, 100, 333], H=8, Hkv=8, D=128, B=16)),
+    ("mha_d64_b32", dict(ctx=[64, 200, 31], H=4, Hkv=4, D=64, B=32)),
+    ("gqa_g4_b64", dict(ctx=[300, 1, 129], H=8, Hkv=2, D=128, B=64)),
+    ("gqa_g8_d64", dict(ctx=[77, 512], H=16, Hkv=2, D=64, B=16)),
+]
+
+
+@pytest.mark.parametrize("qt", ["f16", "bf16"])
+@pytest.mark.parametrize("name,kw", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_decode_fp8_matches_oracle(name, kw, qt):
+    _say(f"fp8 decode {name} {qt}")
+    wl = build(f"fp8_{name}", qt, kw["ctx"], kw["H"], kw["Hkv"], kw["D"], kw["B"], seed=17,
+               pool="choice", pool_factor=1.5, value_scale=0.5, kv_dtype="fp8", kv_scale=0.375)
+    ref = _oracle(wl)
+    for ps in (0, 64, 128):
+        got = _fp8_decode(wl, partition_size=ps)
+        BD.assert_close(got, ref, qt, f"{name} partition {ps}")
+
+
+def test_decode_fp8_invalid_values_poison_only_their_row():
+    _say("fp8 invalid device values")
+    wl = build("fp8_bad", "f16", [40, 50, 60], 4, 4, 128, 16, seed=4, kv_dtype="fp8",
+               kv_scale=0.5)
+    wl.block_tables[1, 2] = wl.num_blocks + 3            # bad id in sequence 1
+    got = _fp8_decode(wl)
+    assert np.isnan(got[1]).all()
+    ref = _oracle(wl, pairs=[(s, h) for s in (0, 2) for h in range(4)])
+    BD.assert_close(got[[0, 2]], ref[[0, 2]], "f16", "good rows")
+
+
+def test_decode_fp8_full_size_sampled():
+    """The LLaMA-7B-shaped fp8 workload at full size, in the bench's launch
+    configuration; outputs checked on a sample of (sequence, head) rows."""
+    _say("fp8 full-size llama7b sampled")
+    wl = make_workload(5)
+    got = _fp8_decode(wl)
+    rng = np.random.default_rng(0)
+    pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, wl.num_seqs, 24),
+                                                rng.integers(0, wl.num_heads, 24))]
+    ref = _oracle(wl, pairs=pairs)
+    idx = tuple(np.array(pairs).T)
+    BD.assert_close(got[idx], ref[idx], "f16", "llama7b fp8 sample")
+    assert np.isfinite(got).all()

@@ -61,6 +61,8 @@ def _encode(x32: np.ndarray, dtype: str) -> np.ndarray:
 
 def nan_bits(dtype: str):
     """The storage word of a quiet NaN in ``dtype``."""
+    if dtype == "fp8":
+        return np.uint8(0x7F)
     if dtype == "f32":
         return np.float32(np.nan)
     if dtype == "f16":
@@ -82,6 +84,40 @@ def normal_array(seed: int, stream: int, shape, dtype: str, scale: float = 1.0,
         if scale != 1.0:
             x *= np.float32(scale)
         out[lo:hi] = _encode(x, dtype)
+
+    if threads is None:
+        threads = min(8, len(os.sched_getaffinity(0)))
+    if nchunks <= 1 or threads <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+# Exponent fields of random E4M3 codes, as a lookup table over 50 equally
+# likely draws: magnitudes mostly within a factor of 8 of 1 (fields 4..8 are
+# 2^-3 .. 2^1), as a normal sample would be.
+_E4M3_EXP_TABLE = np.repeat(np.arange(2, 10, dtype=np.uint8),
+                            [1, 2, 4, 8, 14, 14, 6, 1])          # 50 entries
+
+
+def e4m3_codes(seed: int, stream: int, shape, threads: int | None = None) -> np.ndarray:
+    """Random E4M3 storage codes (uint8): random sign and mantissa bits and an
+    exponent field drawn from ``_E4M3_EXP_TABLE``.  Codes are drawn directly
+    as bit patterns (no value is quantised here); NaN codes never occur.
+    Chunked and seeded per chunk like ``normal_array``."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.uint8)
+    nchunks = (n + CHUNK - 1) // CHUNK
+
+    def fill(c: int) -> None:
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(stream, c))))
+        e = _E4M3_EXP_TABLE[g.integers(0, len(_E4M3_EXP_TABLE), size=hi - lo, dtype=np.uint8)]
+        sm = g.integers(0, 16, size=hi - lo, dtype=np.uint8)       # sign bit | 3 mantissa bits
+        out[lo:hi] = ((sm & 8) << 4) | (e << 3) | (sm & 7)
 
     if threads is None:
         threads = min(8, len(os.sched_getaffinity(0)))
@@ -119,6 +155,13 @@ class Workload:
     cw_key: np.ndarray | None = None     # [T][Hkv][D]
     cw_value: np.ndarray | None = None
     notes: dict = field(default_factory=dict)
+    kv_dtype: str | None = None   # pool storage type when it differs from dtype ("fp8")
+    k_scale: float = 1.0          # fp8 pools: value = code * scale
+    v_scale: float = 1.0
+
+    @property
+    def pool_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -162,7 +205,8 @@ def _poison_unused(wl_key: np.ndarray, wl_val: np.ndarray, tables: np.ndarray,
 def build(name: str, dtype: str, ctx, num_heads: int, num_kv_heads: int, head_dim: int,
           block_size: int, seed: int, pool: str = "permutation", pool_factor: float = 1.0,
           value_scale: float = 1.0, shared_prefix_tokens: int = 0, partition_size: int = 0,
-          num_blocks: int | None = None, cw_tokens: int = 0, notes: dict | None = None) -> Workload:
+          num_blocks: int | None = None, cw_tokens: int = 0, notes: dict | None = None,
+          kv_dtype: str | None = None, kv_scale: float = 1.0) -> Workload:
     """Assemble a workload from sizes.
 
     ``pool``: "permutation" -- ids are consecutive slices of a random
@@ -209,16 +253,21 @@ def build(name: str, dtype: str, ctx, num_heads: int, num_kv_heads: int, head_di
     NB = max(NB, 1)
     H, Hkv, D = num_heads, num_kv_heads, head_dim
     q = normal_array(seed, _STREAM["q"], (S, H, D), dtype, value_scale)
-    kc = normal_array(seed, _STREAM["k"], (NB, Hkv, B, D), dtype, value_scale)
-    vc = normal_array(seed, _STREAM["v"], (NB, Hkv, B, D), dtype, value_scale)
-    _poison_unused(kc, vc, tables, ctx, B, dtype)
+    if kv_dtype == "fp8":
+        kc = e4m3_codes(seed, _STREAM["k"], (NB, Hkv, B, D))
+        vc = e4m3_codes(seed, _STREAM["v"], (NB, Hkv, B, D))
+    else:
+        kc = normal_array(seed, _STREAM["k"], (NB, Hkv, B, D), dtype, value_scale)
+        vc = normal_array(seed, _STREAM["v"], (NB, Hkv, B, D), dtype, value_scale)
+    _poison_unused(kc, vc, tables, ctx, B, kv_dtype or dtype)
     nk = normal_array(seed, _STREAM["new_k"], (S, Hkv, D), dtype, value_scale)
     nv = normal_array(seed, _STREAM["new_v"], (S, Hkv, D), dtype, value_scale)
     wl = Workload(name=name, dtype=dtype, num_seqs=S, num_heads=H, num_kv_heads=Hkv, head_dim=D,
                   block_size=B, num_blocks=NB, context_lens=ctx, block_tables=tables, q=q,
                   key_cache=kc, value_cache=vc, new_key=nk, new_value=nv,
                   scale=1.0 / math.sqrt(D), partition_size=partition_size, seed=seed,
-                  notes=dict(notes or {}))
+                  notes=dict(notes or {}), kv_dtype=kv_dtype,
+                  k_scale=kv_scale if kv_dtype else 1.0, v_scale=kv_scale if kv_dtype else 1.0)
     if cw_tokens:
         wl.cw_slots = rng.choice(NB * B, cw_tokens, replace=False).astype(np.int64)
         wl.cw_key = normal_array(seed, _STREAM["cw_k"], (cw_tokens, Hkv, D), dtype, value_scale)
@@ -238,13 +287,14 @@ CONFIG_NAMES = {
     2: "llama13b_bf16",
     3: "gqa70b_bf16",
     4: "longctx_prefix_f16",
+    5: "llama7b_fp8kv",
 }
 
 
 def make_workload(index: int, seed: int | None = None, block_size: int | None = None,
                   num_seqs: int | None = None, head_scale: int = 1,
                   ctx_override=None) -> Workload:
-    """Workload ``index`` (0..4).  ``seed`` defaults to the index.
+    """Workload ``index`` (0..5).  ``seed`` defaults to the index.
 
     ``num_seqs`` / ``head_scale`` (divide head counts by it) / ``ctx_override``
     shrink a workload for oracle-sized parity runs without changing its
@@ -281,6 +331,14 @@ def make_workload(index: int, seed: int | None = None, block_size: int | None = 
         ctx = [32768] * S if ctx_override is None else ctx_override
         return build(name, "f16", ctx, 32 // head_scale, 32 // head_scale, 128, block_size or 64, seed,
                      pool="permutation", shared_prefix_tokens=2048, partition_size=512)
+    if index == 5:
+        # The LLaMA-7B-shaped layer with 8-bit (E4M3) K/V pools, scale 0.5:
+        # fp16 queries and outputs, random codes in the pools.
+        S = num_seqs or 32
+        ctx = rng.integers(512, 2048 + 1, size=S) if ctx_override is None else ctx_override
+        return build(name, "f16", ctx, 32 // head_scale, 32 // head_scale, 128, block_size or 16, seed,
+                     pool="choice", pool_factor=1.2, value_scale=0.5, kv_dtype="fp8",
+                     kv_scale=0.5)
     raise ValueError(index)
 
 
@@ -290,11 +348,13 @@ def make_workload(index: int, seed: int | None = None, block_size: int | None = 
 
 def torch_dtype(dtype: str):
     import torch
-    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+            "fp8": torch.uint8}[dtype]
 
 
 def to_torch(raw: np.ndarray, dtype: str, device="cpu"):
-    """The raw storage words of ``raw`` as a torch tensor of the storage type."""
+    """The raw storage words of ``raw`` as a torch tensor of the storage type
+    (fp8 codes as uint8)."""
     import torch
     arr = np.ascontiguousarray(raw)
     if dtype == "bf16":
@@ -330,8 +390,8 @@ def to_device(wl: Workload, device="cuda") -> DeviceWorkload:
     q = to_torch(wl.q, wl.dtype, device)
     return DeviceWorkload(
         q=q,
-        key_cache=to_torch(wl.key_cache, wl.dtype, device),
-        value_cache=to_torch(wl.value_cache, wl.dtype, device),
+        key_cache=to_torch(wl.key_cache, wl.pool_dtype, device),
+        value_cache=to_torch(wl.value_cache, wl.pool_dtype, device),
         block_tables=torch.from_numpy(wl.block_tables).to(device),
         context_lens=torch.from_numpy(wl.context_lens).to(device),
         new_key=to_torch(wl.new_key, wl.dtype, device),
