@@ -48,8 +48,8 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
     "llama7b_f16/B16/P4096": {
-        "sources": "025e9042c0c4ce6599e191b107b7c2e5105afa9ab0bfc125181a498ca27cf191",
-        "fetch_kib": 328458.703, "fetch_scale": 1.99992,
+        "sources": "42b4cfaa8549ab29d95fe4be8a7db9c495f202601138c293e44cb5d96ba45a13",
+        "fetch_kib": 328441.547, "fetch_scale": 1048576 / 524311.688,
         "write_kib": 256.0, "write_scale": 1.0,
         "profile": "profiles/decode_mha_llama7b_f16.md"},
 }

@@ -199,12 +199,16 @@ void decode_gqa_kernel(DecodeArgs a) {
     const int off = tok & (a.block_size - 1);
     return ((size_t)phys * block_stride + (size_t)off * D) * E;
   };
-  auto load = [&](u32x4 *kb, u32x4 *vb, int k) {
-    const size_t off = chunk_offset(k);
+  // Chunks past the wave's last one (the pipeline's run-out) are loaded
+  // through an empty descriptor: such loads return zeros without touching
+  // memory, and their registers are never consumed.
+  auto load = [&](u32x4 *kb, u32x4 *vb, int k, int last) {
+    const size_t off = chunk_offset(min(k, last));
+    const int range = k <= last ? kChunkBytes : 0;
     const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, kChunkBytes, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, range, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, kChunkBytes, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, range, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < VL; ++j)
       kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, v_off + j * TPL * ROW, 0, kStreamPolicy);
@@ -309,13 +313,13 @@ void decode_gqa_kernel(DecodeArgs a) {
   u32x4 kb[NBUF][VL], vb[NBUF][VL];
   if (nch_w > 0) {
     const int last = nch_w - 1;
-    load(kb[0], vb[0], 0);
+    load(kb[0], vb[0], 0, last);
     for (int k0 = 0; k0 < nch_w; k0 += NBUF) {
 #pragma unroll
       for (int i = 0; i < NBUF; ++i) {
         const int k = k0 + i;
         if (k >= nch_w) break;
-        load(kb[(i + 1) % NBUF], vb[(i + 1) % NBUF], min(k + 1, last));
+        load(kb[(i + 1) % NBUF], vb[(i + 1) % NBUF], k + 1, last);
         consume(kb[i], vb[i], k);
       }
     }

@@ -224,12 +224,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   // every lane then needs only its 32-bit offset, and nothing outside the
   // chunk can be touched.
   constexpr int kChunkBytes = kChunk * D * E;
-  auto load = [&](u32x4 *kb, u32x4 *vb, int k) {
-    const size_t off = chunk_offset(k);
+  // Chunks past the wave's last one (the pipeline's run-out) are loaded
+  // through an empty descriptor: such loads return zeros without touching
+  // memory, and their registers are never consumed.
+  auto load = [&](u32x4 *kb, u32x4 *vb, int k, int last) {
+    const size_t off = chunk_offset(min(k, last));
+    const int range = k <= last ? kChunkBytes : 0;
     const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, kChunkBytes, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, range, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, kChunkBytes, kBufferFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, range, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < NL; ++j)
       kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + j * TPL * D * E, 0, kStreamPolicy);
@@ -279,20 +283,20 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   };
 
   // Software pipeline over NBUF register buffers: while chunk k is consumed,
-  // chunks k+1 .. k+NBUF-1 are in flight.  Loads past the last chunk are
-  // clamped to it (L2 hits, never consumed).
-  constexpr int NBUF = kDecodeBuffers;
+  // chunks k+1 .. k+NBUF-1 are in flight.  Loads past the last chunk go
+  // through an empty descriptor (see load).
+  constexpr int NBUF = KT == kFP8 ? kDecodeBuffersFp8 : kDecodeBuffers;
   u32x4 kb[NBUF][NL], vb[NBUF][NL];
   if (nch_w > 0) {
     const int last = nch_w - 1;
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) load(kb[i], vb[i], min(i, last));
+    for (int i = 0; i < NBUF - 1; ++i) load(kb[i], vb[i], i, last);
     for (int k0 = 0; k0 < nch_w; k0 += NBUF) {
 #pragma unroll
       for (int i = 0; i < NBUF; ++i) {
         const int k = k0 + i;
         if (k >= nch_w) break;
-        load(kb[(i + NBUF - 1) % NBUF], vb[(i + NBUF - 1) % NBUF], min(k + NBUF - 1, last));
+        load(kb[(i + NBUF - 1) % NBUF], vb[(i + NBUF - 1) % NBUF], k + NBUF - 1, last);
         consume(kb[i], vb[i], k);
       }
     }

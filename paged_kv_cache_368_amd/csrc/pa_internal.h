@@ -35,6 +35,10 @@ constexpr int kDecodeWaves = PA_DECODE_WAVES;   // waves per decode work-group
 #define PA_DECODE_BUFFERS 2
 #endif
 constexpr int kDecodeBuffers = PA_DECODE_BUFFERS; // K/V chunk buffers in flight per wave
+#ifndef PA_DECODE_BUFFERS_FP8
+#define PA_DECODE_BUFFERS_FP8 2
+#endif
+constexpr int kDecodeBuffersFp8 = PA_DECODE_BUFFERS_FP8;  // the same for 8-bit pools
 #ifndef PA_GQA_WAVES
 #define PA_GQA_WAVES 4
 #endif
