@@ -148,7 +148,38 @@ def _fp8_decode_no_v_scale(q, kc, vc, bt, cl, b, scale, qd, ks, vs, hkv=None, pa
     return _orig["paged_decode_fp8"](q, kc, vc, bt, cl, b, scale, qd, ks, 1.0, hkv, pairs)
 
 
+def _prefill_top_left(q, kc, vc, bt, cl, qs, b, scale, dtype, hkv=None, rows=None):
+    cl2 = np.array([int(qs[s + 1]) - int(qs[s]) for s in range(len(cl))], np.int32)
+    return _orig["paged_prefill"](q, kc, vc, bt, cl2, qs, b, scale, dtype, hkv, rows)
+
+
+def _prefill_not_causal(q, kc, vc, bt, cl, qs, b, scale, dtype, hkv=None, rows=None):
+    T = q.shape[0]
+    qs2 = np.arange(T + 1) * 0
+    out = np.empty((T,) + q.shape[1:])
+    for s in range(len(cl)):
+        for i in range(int(qs[s]), int(qs[s + 1])):
+            out[i] = _orig["paged_decode"](q[i:i + 1], kc, vc, bt[s:s + 1], cl[s:s + 1], b, scale,
+                                           dtype, hkv)[0]
+    return out
+
+
+def _prefill_pos_plus_one(q, kc, vc, bt, cl, qs, b, scale, dtype, hkv=None, rows=None):
+    T, H, D = q.shape
+    out = np.full((T, H, D), np.nan)
+    Hk = kc.shape[1] if hkv is None else hkv
+    for s in range(len(cl)):
+        L = int(qs[s + 1]) - int(qs[s])
+        for j in range(L):
+            n = min(int(cl[s]) - L + j + 2, int(cl[s]))
+            for h in range(H):
+                out[int(qs[s]) + j, h] = P.decode_one(P.to_f64(q[int(qs[s]) + j, h], dtype), kc, vc,
+                                                      bt[s], n, P.kv_head_of(h, H, Hk), b, scale, dtype)
+    return out
+
+
 MUTANTS = {
+    "paged_prefill": [_prefill_top_left, _prefill_not_causal, _prefill_pos_plus_one],
     "e4m3_decode": [_e4m3_bias8, _e4m3_no_subnormals],
     "e4m3_encode": [_e4m3_truncate, _e4m3_ties_up],
     "quantize_e4m3": [_quantize_times_scale],

@@ -513,3 +513,79 @@ def test_pin_fp8_cache_write_quantises_with_pool_scale():
     touched = np.zeros((NB, B), bool)
     touched[5 // B, 5 % B] = touched[22 // B, 22 % B] = True
     assert (kc.transpose(0, 2, 1, 3)[~touched] == 0x55).all()
+
+
+# --------------------------------------------------------------------------
+# Paged prefill
+# --------------------------------------------------------------------------
+
+def _prefill_case(seed, ctx, qlens, H, Hkv, D, B, dtype="f32"):
+    rng = _rng(seed)
+    S = len(ctx)
+    nb = [P.num_required_blocks(c, B) for c in ctx]
+    NB = sum(nb) + 3
+    perm = rng.permutation(NB)
+    MB = max(nb)
+    tables = np.full((S, MB), -1, np.int32)
+    pos = 0
+    for s in range(S):
+        tables[s, :nb[s]] = perm[pos:pos + nb[s]]
+        pos += nb[s]
+    kc = rng.standard_normal((NB, Hkv, B, D)).astype(np.float32)
+    vc = rng.standard_normal((NB, Hkv, B, D)).astype(np.float32)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = rng.standard_normal((int(qs[-1]), H, D)).astype(np.float32)
+    return kc, vc, tables, np.array(ctx, np.int32), qs, q
+
+
+def _contiguous(cache, table, n, B):
+    return np.stack([cache[table[t // B], :, t % B, :] for t in range(n)])   # [n][Hkv][D]
+
+
+def test_pin_prefill_fresh_prompts_are_causal_sdpa():
+    """A whole prompt as queries (qlen = ctx) is causal attention over the
+    contiguous sequence: the library routine with is_causal (float64), with
+    kv heads repeated for grouped queries."""
+    B, H, Hkv, D = 4, 4, 2, 8
+    ctx = [9, 1, 13]
+    kc, vc, tables, cl, qs, q = _prefill_case(40, ctx, ctx, H, Hkv, D, B)
+    got = P.paged_prefill(q, kc, vc, tables, cl, qs, B, 0.4, "f32")
+    G = H // Hkv
+    for s, n in enumerate(ctx):
+        K = torch.tensor(_contiguous(kc, tables[s], n, B).astype(np.float64)).repeat_interleave(G, 1)
+        V = torch.tensor(_contiguous(vc, tables[s], n, B).astype(np.float64)).repeat_interleave(G, 1)
+        Q = torch.tensor(q[qs[s]:qs[s + 1]].astype(np.float64))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            Q.transpose(0, 1), K.transpose(0, 1), V.transpose(0, 1), is_causal=True,
+            scale=0.4).transpose(0, 1).numpy()
+        assert np.abs(got[qs[s]:qs[s + 1]] - ref).max() < 1e-12
+
+
+def test_pin_prefill_suffix_after_cached_prefix():
+    """Queries for only the last qlen tokens (the prefix is already cached, as
+    with a shared prefix): row j attends to tokens 0 .. ctx - qlen + j, the
+    library routine with that explicit mask."""
+    B, H, Hkv, D = 8, 2, 2, 16
+    ctx, qlens = [40, 17, 64], [5, 17, 1]
+    kc, vc, tables, cl, qs, q = _prefill_case(41, ctx, qlens, H, Hkv, D, B)
+    got = P.paged_prefill(q, kc, vc, tables, cl, qs, B, 0.25, "f32")
+    for s, (n, L) in enumerate(zip(ctx, qlens)):
+        K = torch.tensor(_contiguous(kc, tables[s], n, B).astype(np.float64)).transpose(0, 1)
+        V = torch.tensor(_contiguous(vc, tables[s], n, B).astype(np.float64)).transpose(0, 1)
+        Q = torch.tensor(q[qs[s]:qs[s + 1]].astype(np.float64)).transpose(0, 1)
+        mask = torch.tensor([[t <= n - L + j for t in range(n)] for j in range(L)])
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask,
+                                                               scale=0.25).transpose(0, 1).numpy()
+        assert np.abs(got[qs[s]:qs[s + 1]] - ref).max() < 1e-12
+
+
+def test_pin_prefill_last_row_is_decode():
+    """The last query row of a sequence is the decode output for that
+    sequence (same context)."""
+    B, H, Hkv, D = 4, 4, 4, 8
+    ctx, qlens = [11, 30], [3, 30]
+    kc, vc, tables, cl, qs, q = _prefill_case(42, ctx, qlens, H, Hkv, D, B)
+    got = P.paged_prefill(q, kc, vc, tables, cl, qs, B, 0.3, "f32")
+    last = q[qs[1:] - 1]                                        # [S][H][D]
+    dec = P.paged_decode(last, kc, vc, tables, cl, B, 0.3, "f32")
+    assert np.array_equal(got[qs[1:] - 1], dec)
