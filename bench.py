@@ -201,6 +201,73 @@ def bench_copy_blocks(args) -> dict:
     }
 
 
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
+
+
+def prefill_flops(context_lens, query_lens, num_heads, head_dim) -> int:
+    """Algorithmic flops of causal prefill: each (query row, head) at position
+    p does 2*D flops for q.k and 2*D for p*V with each of its p + 1 keys."""
+    total = 0
+    for n, L in zip(context_lens, query_lens):
+        first = int(n) - int(L)
+        total += sum(first + j + 1 for j in range(int(L)))
+    return 4 * head_dim * num_heads * total
+
+
+def bench_prefill(args) -> dict:
+    """pa_prefill on LLaMA-7B-shaped prompts (32 heads of 128, fp16, blocks of
+    16): 8 sequences of 2048 tokens, either whole fresh prompts or the last
+    512 tokens after a 1536-token cached prefix (--prefix)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_368_amd as pa
+    from workloads import build, normal_array, to_torch
+
+    S, H, D, B, n = 8, 32, 128, 16, 2048
+    L = n - args.prefix
+    wl = build("llama7b_prefill_f16", "f16", [n] * S, H, H, D, B, seed=7, pool="permutation",
+               value_scale=0.5)
+    qs = np.arange(S + 1, dtype=np.int32) * L
+    q = to_torch(normal_array(7, 40, (S * L, H, D), "f16", 0.5), "f16", "cuda")
+    kc, vc = to_torch(wl.key_cache, "f16", "cuda"), to_torch(wl.value_cache, "f16", "cuda")
+    bt = torch.tensor(wl.block_tables, device="cuda")
+    cl = torch.tensor(wl.context_lens, device="cuda")
+    qst = torch.tensor(qs, device="cuda")
+    out = torch.empty_like(q)
+    flops = prefill_flops(wl.context_lens, [L] * S, H, D)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        pa.pa_prefill(out, q, kc, vc, bt, cl, qst, L, n, wl.scale)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        pa.pa_prefill(out, q, kc, vc, bt, cl, qst, L, n, wl.scale)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e-3
+    tflops = flops / mean / 1e12
+    return {
+        "metric": "paged prefill (pa_prefill): query tokens/s and causal attention TFLOP/s",
+        "value": S * L / mean, "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1)*0.5 q/K/V, random block tables)",
+        "config": {"workload": "llama7b_prefill_f16", "num_seqs": S, "num_heads": H,
+                   "head_dim": D, "block_size": B, "context_len": n, "query_len": L,
+                   "cached_prefix": args.prefix},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS["f16"],
+                     "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"], "traffic": None,
+                     "kernel": "prefill_kernel", "flops_per_launch": flops,
+                     "mean_launch_us": mean * 1e6},
+        "cpu_baseline": None,
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,8 +279,10 @@ def main(argv=None) -> int:
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["decode", "copy_blocks"], default="decode",
-                    help="decode (the headline step, default) or whole-block copies")
+    ap.add_argument("--op", choices=["decode", "copy_blocks", "prefill"], default="decode",
+                    help="decode (the headline step, default), whole-block copies, or prefill")
+    ap.add_argument("--prefix", type=int, default=0,
+                    help="--op prefill: tokens of each 2048-token prompt already cached")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs for --op copy_blocks")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
@@ -233,6 +302,9 @@ def main(argv=None) -> int:
     pa.load_library()
     if args.op == "copy_blocks":
         print(json.dumps(bench_copy_blocks(args)), flush=True)
+        return 0
+    if args.op == "prefill":
+        print(json.dumps(bench_prefill(args)), flush=True)
         return 0
     dev_name = torch.cuda.get_device_name(0)
     print(f"[bench] device {dev_name}; building workload {args.config}", file=sys.stderr, flush=True)

@@ -179,6 +179,46 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
                       pa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * pa_prefill -- paged attention for many query tokens per sequence (a prompt,
+ * or the new part of a prompt whose prefix is already cached), on the matrix
+ * cores.  The pages give the per-token step (P2 §2.1: the token's K/V join
+ * the cache, then its query attends over every cached K/V) and say that a
+ * cached shared prefix spares its prefill work (P3 §3); this is that step
+ * for every prompt token:
+ *
+ *   out[i][h] = softmax(scale * q[i][h] . K_s[0..p]^T) V_s[0..p]
+ *
+ * where row i is the j-th query row of sequence s (query_start[s] <= i <
+ * query_start[s+1], j = i - query_start[s]), qlen = query_start[s+1] -
+ * query_start[s], and p = context_lens[s] - qlen + j: the queries are the
+ * last qlen tokens of the context, whose K/V the caller has already written
+ * (pa_cache_write), and each attends causally to the tokens up to its own.
+ *
+ *   out            out  [num_tokens][num_heads][head_dim], dtype
+ *   q              in   [num_tokens][num_heads][head_dim], dtype
+ *   key_cache, value_cache, block_tables, num_blocks, max_blocks_per_seq:
+ *                       as for pa_decode
+ *   context_lens   in   int32 [num_seqs]: tokens in the cache, queries included
+ *   query_start    in   int32 [num_seqs + 1], non-decreasing, query_start[0]
+ *                       = 0, query_start[num_seqs] = num_tokens
+ *   max_query_len       host-side upper bound on every qlen (<= max_context_len)
+ *
+ * Rows of a sequence whose device values are inconsistent (context length
+ * negative or above max_context_len or max_blocks_per_seq * block_size; qlen
+ * negative, above its context or above max_query_len; query_start outside
+ * [0, num_tokens]), or whose used table entries fall outside [0, num_blocks),
+ * get NaN; other sequences are unaffected.  Supported: fp16, bf16; head_dim
+ * 64 or 128; block_size 16, 32 or 64; num_heads % num_kv_heads == 0.
+ */
+pa_status_t pa_prefill(void *out, const void *q, const void *key_cache, const void *value_cache,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       const int32_t *query_start, int32_t num_seqs, int32_t num_tokens,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_query_len, int32_t max_context_len, float scale,
+                       pa_dtype_t dtype, hipStream_t stream);
+
+/*
  * pa_cache_write_fp8 -- pa_cache_write into E4M3 pools.  The pages advise
  * keeping the cache in a lower precision to save memory (P1 §4 keeps blocks
  * in bfloat16; P1 §5 and P2 §5 quantise and compress the cache); this build's

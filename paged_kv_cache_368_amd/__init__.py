@@ -20,5 +20,6 @@ from ._capi import (  # noqa: F401
     pa_decode_partition_size,
     pa_decode_workspace_size,
     pa_last_error,
+    pa_prefill,
     pa_version,
 )

@@ -343,6 +343,62 @@ pa_status_t pa_decode_fp8(void *out, const void *q, const void *key_cache,
                      partition_size, workspace, workspace_bytes, q_dtype, PA_FP8_E4M3, stream);
 }
 
+pa_status_t pa_prefill(void *out, const void *q, const void *key_cache, const void *value_cache,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       const int32_t *query_start, int32_t num_seqs, int32_t num_tokens,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_query_len, int32_t max_context_len, float scale,
+                       pa_dtype_t dtype, hipStream_t stream) {
+  pa_status_t st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                               max_context_len, dtype);
+  if (st != PA_OK) return st;
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill takes fp16 or bf16");
+  if (num_tokens < 0 || max_query_len < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens and max_query_len must be >= 0");
+  if (max_query_len > max_context_len)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_query_len exceeds max_context_len");
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks and max_blocks_per_seq must be > 0");
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "max_context_len exceeds max_blocks_per_seq * block_size");
+  if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens || !query_start)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pointer arguments must not be NULL");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "out, q and the pools must be 16-byte aligned");
+  const long long tiles = ceil_div(max_query_len, pa::prefill_rows_per_tile());
+  if ((long long)num_seqs * num_heads * tiles > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "too many (sequence, head, query tile) work items");
+  pa::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = key_cache;
+  a.v_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.log2_block = ilog2(block_size);
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.max_context_len = max_context_len;
+  a.num_tiles = (int)tiles;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pa::launch_prefill(a, dtype, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
 pa_status_t pa_cache_write_fp8(const void *key, const void *value, void *key_cache,
                                void *value_cache, const int64_t *slot_mapping,
                                int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,

@@ -63,6 +63,25 @@ struct DecodeArgs {
 };
 
 // kv_dt: the pools' storage type, equal to dt or kFP8 (dt fp16/bf16 only).
+struct PrefillArgs {
+  void *out;                 // [T][H][D]
+  const void *q;             // [T][H][D]
+  const void *k_cache;       // [NB][Hkv][B][D]
+  const void *v_cache;
+  const int32_t *block_tables;  // [S][MB]
+  const int32_t *context_lens;  // [S]
+  const int32_t *query_start;   // [S + 1]
+  int num_seqs, num_tokens, num_heads, num_kv_heads, head_dim;
+  int block_size, log2_block, num_blocks, max_blocks_per_seq;
+  int max_query_len, max_context_len;
+  int num_tiles;             // ceil(max_query_len / rows per tile)
+  float scale_log2;
+};
+
+// Paged prefill on the matrix cores: fp16/bf16, head_dim 64 or 128.
+int prefill_rows_per_tile();
+hipError_t launch_prefill(const PrefillArgs &a, int dt, hipStream_t stream);
+
 hipError_t launch_decode_mha(const DecodeArgs &a, int dt, int kv_dt, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs &a, int dt, hipStream_t stream);
 
