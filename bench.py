@@ -142,6 +142,41 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
                       f"{tokens} head-tokens in {el:.1f} s, float64 numpy, 1 thread on {cpu}"}
 
 
+def _cpu_name() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _timed_oracle(fn, items, budget_s: float):
+    """Run ``fn(item)`` over ``items`` in order, single-threaded, until the
+    time budget is spent; returns (items done, seconds)."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                                    # pragma: no cover
+        threadpool_limits = None
+    ctx_mgr = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx_mgr:
+        ctx_mgr.__enter__()
+    try:
+        done = 0
+        t0 = time.perf_counter()
+        for it in items:
+            fn(it)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        return done, time.perf_counter() - t0
+    finally:
+        if ctx_mgr:
+            ctx_mgr.__exit__(None, None, None)
+
+
 def bench_copy_blocks(args) -> dict:
     """Whole-block copies (pa_copy_blocks) on LLaMA-13B-shaped bf16 pools
     (40 kv heads x 16 tokens x 128 dims = 160 KB per block and pool):
@@ -197,8 +232,33 @@ def bench_copy_blocks(args) -> dict:
                      "unit": "GB/s", "frac": moved / t_cow / 1e9 / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": "copy_blocks_kernel (copy on write)"},
         "swap_out_gbps": one_way / t_out / 1e9, "swap_in_gbps": one_way / t_in / 1e9,
-        "swap_out_us": t_out * 1e6, "swap_in_us": t_in * 1e6, "cpu_baseline": None,
+        "swap_out_us": t_out * 1e6, "swap_in_us": t_in * 1e6,
+        "cpu_baseline": None if args.no_cpu_baseline else _copy_cpu_baseline(Hkv, B, D, npairs),
     }
+
+
+def _copy_cpu_baseline(Hkv, B, D, npairs) -> dict:
+    """The oracle's block copy on host pools of the same block shape: copy
+    on write of the first pairs of a random pairing, bytes read + written."""
+    import numpy as np
+
+    import oracle.paged as P
+
+    NB = 2 * npairs
+    rng = np.random.default_rng(11)
+    kc = rng.integers(0, 65535, (NB, Hkv, B, D), dtype=np.uint16)
+    vc = rng.integers(0, 65535, (NB, Hkv, B, D), dtype=np.uint16)
+    perm = rng.permutation(NB)
+    pairs = list(zip(perm[:npairs].tolist(), perm[npairs:].tolist()))
+
+    def one(pair):
+        P.copy_blocks(kc, kc, [pair])
+        P.copy_blocks(vc, vc, [pair])
+
+    done, el = _timed_oracle(one, pairs, 10.0)
+    moved = 2 * 2 * done * Hkv * B * D * 2
+    return {"value": moved / el / 1e9, "unit": "GB/s (read+write)", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {npairs} block pairs (K and V), numpy, 1 thread on {_cpu_name()}"}
 
 
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
@@ -264,8 +324,33 @@ def bench_prefill(args) -> dict:
                      "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"], "traffic": None,
                      "kernel": "prefill_kernel", "flops_per_launch": flops,
                      "mean_launch_us": mean * 1e6},
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else _prefill_cpu_baseline(wl, qs, args.prefix),
     }
+
+
+def _prefill_cpu_baseline(wl, qs, prefix) -> dict:
+    """The float64 oracle's prefill on (row, head) pairs of the same workload
+    in order, single-threaded, for up to ~12 s; reported as query tokens/s
+    (a query token covers all heads)."""
+    import numpy as np
+
+    import oracle.paged as P
+    from workloads import normal_array
+
+    q = normal_array(7, 40, (int(qs[-1]), wl.num_heads, wl.head_dim), "f16", 0.5)
+    items = [(i, h) for i in range(int(qs[-1])) for h in range(wl.num_heads)]
+    order = np.random.default_rng(0).permutation(len(items))     # a representative mix of rows
+    items = [items[k] for k in order]
+
+    def one(item):
+        P.paged_prefill(q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens, qs,
+                        wl.block_size, wl.scale, wl.dtype, wl.num_kv_heads, rows=[item])
+
+    done, el = _timed_oracle(one, items, 12.0)
+    return {"value": done / wl.num_heads / el, "unit": "query tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} of {len(items)} (query row, head) pairs in seeded random order, "
+                      f"{prefix}-token cached prefix, float64 numpy, 1 thread on {_cpu_name()}"}
 
 
 def main(argv=None) -> int:
