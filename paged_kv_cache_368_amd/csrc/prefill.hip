@@ -7,21 +7,30 @@
 // found through block_tables[s] (P3 §2-§3).  A prefix cached earlier (P3 §3,
 // shared prefixes save prefill work) is simply not among the queries.
 //
-// Work decomposition: one work-group of NW waves per (sequence, 16-row query
-// tile, query head); waves take 16-token chunks of the context round-robin.
-// The products are the grouped-query decode kernel's, with the 16 query rows
-// of the tile as the N side:
+// Work decomposition: one work-group of 4 waves per (sequence, 64-row query
+// tile, query head); wave w owns rows 16w .. 16w+15 of the tile, so each
+// wave holds the complete softmax state of its rows and no cross-wave merge
+// is needed.  The work-group walks the context in 32-token chunks that all
+// four waves share:
 //
-//   S^T[t][r] = sum_d K[t][d] Q[r][d]      v_mfma_f32_16x16x32  (D/32 of them)
-//   O[r][d]  += sum_t P[r][t] V[t][d]      v_mfma_f32_16x16x16  (D/16 tiles)
-//
-// K and V are read with contiguous 1 KB non-temporal wave loads and reach
-// the operand layouts through a per-wave LDS tile (K: 16-byte A-layout reads;
-// V: ds_read_b64_tr_b16 transposed reads).  Column r carries its own causal
-// limit p_r; the mask is applied only on chunks that reach past the tile's
-// first position.  The context is streamed in windows of 4096 tokens whose
-// block ids are staged in LDS; the online softmax (lazy reference max, as in
-// the decode kernel) carries across windows, so no merge pass is needed.
+//   * K and V of a chunk go from HBM straight into LDS (buffer loads with
+//     the LDS bit: no registers), each wave moving a quarter of it, into one
+//     of two stages, so the next chunk streams in while this one is used.
+//     Rows are stored with their 16-byte pieces XOR-swizzled by the row index,
+//     which makes both operand reads below conflict-free.
+//   * S^T = K Q^T: two v_mfma_f32_16x16x32 tiles (tokens 0-15 and 16-31 as M,
+//     the wave's 16 rows as N), K read in the A layout.
+//   * O += P V on v_mfma_f32_16x16x32 with the 32 tokens as the contraction:
+//     a lane's 8 weights are tokens 4g..4g+3 of each token tile, which is the
+//     first product's output layout, and the matching V values come from two
+//     ds_read_b64_tr_b16 reads (one per token tile).  fp16 feeds P rounded to
+//     fp16; bf16 feeds P as a truncated high part plus the remainder (two
+//     products), keeping ~16 significant bits per weight.
+//   * Online softmax per row with the lazy reference max of the decode
+//     kernels; the causal limit of each row is applied on chunks that reach
+//     past the wave's first position, and waves skip chunks that lie wholly
+//     after their rows.
+// Block ids are staged in LDS per 4096-token window.
 #include "pa_mfma.h"
 
 namespace pa {
@@ -30,29 +39,52 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyMax = 8.f;          // log2 units: weights stay <= 256
-constexpr int kRows = 16;                // query rows per work-group
+constexpr int kPfWaves = 4;
+constexpr int kRows = 16 * kPfWaves;     // query rows per work-group
+constexpr int kCh = 32;                  // tokens per chunk
 constexpr int kWindow = kMaxPartition;   // tokens whose block ids are staged at once
+// s_waitcnt immediate for vmcnt(0) (expcnt and lgkmcnt left at their
+// maxima): the wave's own loads, the LDS-bound ones included, have landed.
+constexpr int kWaitVmcnt0 = 0x0f70;
 
-template <int DT, int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)))
-void prefill_kernel(PrefillArgs a) {
+// fp32 weights (a, b) as packed 16-bit values for the A operand.
+template <int DT>
+__device__ __forceinline__ uint32_t pack_p(float a, float b) {
+  if constexpr (DT == kF16) {
+    const _Float16 x = (_Float16)a, y = (_Float16)b;                  // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  } else {
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a),
+                                 0x07060302u);                         // truncated high halves
+  }
+}
+
+// Remainders a - hi(a), b - hi(b) of the bf16 high parts, packed likewise.
+__device__ __forceinline__ uint32_t pack_lo_bf16(float a, float b) {
+  const float ra = a - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xffff0000u);
+  const float rb = b - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, b) & 0xffff0000u);
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, rb), __builtin_bit_cast(uint32_t, ra),
+                               0x07060302u);
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
-  static_assert(NW * 64 >= kMaxPartBlocks, "one thread per staged block id");
+  static_assert(kPfWaves * 64 >= kMaxPartBlocks, "one thread per staged block id");
   constexpr int E = 2;
   constexpr int ROW = D * E;                 // bytes per token row
-  constexpr int PITCH = ROW + 32;            // LDS row pitch: 16-byte rows, spread banks
+  constexpr int PIECES = ROW / 16;           // 16-byte pieces per row
+  constexpr int RPL = 1024 / ROW;            // rows per 1 KB wave load
+  constexpr int LPW = kCh * ROW / 1024 / kPfWaves;   // loads per wave per operand and chunk
   constexpr int KI = D / 32;                 // first-product steps
   constexpr int NT = D / 16;                 // output tiles of 16 dims
-  constexpr int LPT = ROW / 16;              // lanes per row for the wave loads
-  constexpr int TPL = 64 / LPT;              // rows per wave load
-  constexpr int VL = kChunk / TPL;           // loads per chunk and operand
+  constexpr int STAGE = kCh * ROW;           // bytes of one operand in one stage
 
   __shared__ int s_tbl[kMaxPartBlocks];
-  constexpr int kTileBytes = kChunk * PITCH;
-  constexpr int kMergeBytes = NW * kRows * (D + 2) * 4;
-  constexpr int kLdsBytes =
-      (2 * NW * kTileBytes > kMergeBytes) ? 2 * NW * kTileBytes : kMergeBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char s_buf[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_k0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_v0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_k1[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_v1[STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -64,7 +96,8 @@ void prefill_kernel(PrefillArgs a) {
   const int G = H / a.num_kv_heads;
   const int item = blockIdx.x;
   const int h = item % H;
-  const int tile = (item / H) % a.num_tiles;
+  // Tiles with more rows of context first: they take longest.
+  const int tile = a.num_tiles - 1 - (item / H) % a.num_tiles;
   const int s = item / (H * a.num_tiles);
   const int kvh = h / G;
   const int r0 = tile * kRows;
@@ -77,8 +110,7 @@ void prefill_kernel(PrefillArgs a) {
                    qlen > a.max_query_len || q0 < 0 || q1 > a.num_tokens;
   const float nan = __builtin_nanf("");
   if (bad) {
-    // Rows of this tile that lie in the sequence's range and in the output.
-    for (int idx = tid; idx < kRows * D; idx += NW * 64) {
+    for (int idx = tid; idx < kRows * D; idx += kPfWaves * 64) {
       const int r = idx / D, d = idx - r * D;
       const long long row = (long long)q0 + r0 + r;
       if (row >= 0 && row < q1 && row < a.num_tokens)
@@ -90,19 +122,23 @@ void prefill_kernel(PrefillArgs a) {
   const int nrows = min(kRows, qlen - r0);
   const int pos0 = ctx - qlen + r0;          // position of the tile's first row
   const int t1 = pos0 + nrows;               // tokens the tile attends to
-  const int cpos = pos0 + min(c16, nrows - 1);   // causal limit of column c16
+  // This wave's rows: wr0 .. wr0 + wrows - 1 of the tile (wrows may be 0).
+  const int wr0 = 16 * wave;
+  const int wrows = max(0, min(16, nrows - wr0));
+  const int wpos0 = pos0 + wr0;              // position of the wave's first row
+  const int wlast = pos0 + wr0 + max(wrows, 1) - 1;
+  const int cpos = pos0 + wr0 + min(c16, max(wrows, 1) - 1);   // causal limit of column c16
 
-  // Q fragments (B layout: lane l holds row l%16, dims 32i + 8*(l/16) ..+7);
-  // columns past the tile's rows are zero and never stored.
   u32x4 qf[KI];
   {
-    const bool live = c16 < nrows;
+    const bool live = c16 < wrows;
     const char *qrow = reinterpret_cast<const char *>(a.q) +
-                       ((size_t)(q0 + r0 + (live ? c16 : 0)) * H + h) * ROW;
+                       ((size_t)(q0 + r0 + wr0 + (live ? c16 : 0)) * H + h) * ROW;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(qrow + 64 * i + 16 * g4);
-      qf[i] = live ? v : u32x4{0u, 0u, 0u, 0u};
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (live) v = *reinterpret_cast<const u32x4 *>(qrow + 64 * i + 16 * g4);
+      qf[i] = v;
     }
   }
 
@@ -110,13 +146,26 @@ void prefill_kernel(PrefillArgs a) {
   const size_t block_stride = head_stride * a.num_kv_heads;
   const char *kbase = reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E;
   const char *vbase = reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E;
-  const int v_row = lane / LPT, v_col = lane % LPT;
-  const int v_off = v_row * ROW + 16 * v_col;
-  constexpr int kChunkBytes = kChunk * ROW;
 
-  unsigned char *ktile = s_buf + wave * 2 * kTileBytes;
-  unsigned char *tile_v = ktile + kTileBytes;
-  const unsigned char *tr_base = tile_v + (4 * g4 + c16 / 4) * PITCH + 8 * (c16 % 4);
+  // DMA addressing: lane l of a 1 KB load lands at LDS byte 16l of it, i.e.
+  // row l / PIECES, physical piece l % PIECES, which holds logical piece
+  // (l % PIECES) ^ (row % PIECES).
+  const int dma_row = lane / PIECES;                         // row within the load
+  const int dma_pp = lane % PIECES;
+
+  // Operand reads.  K (A layout, token tile tt): row 16tt + c16, logical
+  // piece 4i + g4.  V (transposed reads, token tile tt, dims 16n..): row
+  // 16tt + 4g4 + c16/4, logical byte 32n + 8(c16%4).
+  auto k_addr = [&](int tt, int i) -> int {
+    const int row = 16 * tt + c16;
+    return row * ROW + (((4 * i + g4) ^ (row % PIECES)) << 4);
+  };
+  auto v_addr = [&](int tt, int n) -> int {
+    const int row = 16 * tt + 4 * g4 + c16 / 4;
+    const int lb = 32 * n + 8 * (c16 % 4);
+    return row * ROW + (((lb >> 4) ^ (row % PIECES)) << 4) + (lb & 15);
+  };
+
   float m = kNegInf, l = 0.f;
   f32x4 o[NT];
 #pragma unroll
@@ -126,7 +175,7 @@ void prefill_kernel(PrefillArgs a) {
   for (int w0 = 0; w0 < t1; w0 += kWindow) {
     const int wend = min(t1, w0 + kWindow);
     const int nblk = (wend - w0 + a.block_size - 1) >> a.log2_block;
-    __syncthreads();                          // the previous window's ids are consumed
+    __syncthreads();                          // the previous window is fully consumed
     bool bad_id = false;
     if (tid < nblk) {
       const int id = a.block_tables[(size_t)s * a.max_blocks_per_seq + (w0 >> a.log2_block) + tid];
@@ -137,69 +186,67 @@ void prefill_kernel(PrefillArgs a) {
       poison = true;
       break;
     }
-    const int nch = (wend - w0 + kChunk - 1) / kChunk;
-    const int nch_w = nch > wave ? (nch - wave + NW - 1) / NW : 0;
-    int my_ids = 0;
-    if (lane < nch_w) my_ids = s_tbl[((wave + NW * lane) * kChunk) >> a.log2_block];
+    const int nch = (wend - w0 + kCh - 1) / kCh;
 
-    auto chunk_offset = [&](int k) -> size_t {
-      const int phys = __builtin_amdgcn_readlane(my_ids, k);
-      const int tok = (wave + NW * k) * kChunk;
-      const int off = tok & (a.block_size - 1);
-      return ((size_t)phys * block_stride + (size_t)off * D) * E;
-    };
-    // Run-out chunks past the wave's last one load through an empty
-    // descriptor (zeros, no memory access) and are never consumed.
-    auto load = [&](u32x4 *kb, u32x4 *vb, int k, int last) {
-      const size_t off = chunk_offset(min(k, last));
-      const int range = k <= last ? kChunkBytes : 0;
-      const __amdgpu_buffer_rsrc_t kr =
-          __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, range, kBufferFlags);
-      const __amdgpu_buffer_rsrc_t vr =
-          __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, range, kBufferFlags);
+    // Issue this wave's share of chunk k into stage (sk, sv).  Rows at or
+    // past wend load through an empty range (zeros; their weights are zero).
+    auto dma = [&](int k, unsigned char *sk, unsigned char *sv) {
+      const int tc = w0 + k * kCh;
 #pragma unroll
-      for (int j = 0; j < VL; ++j)
-        kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, v_off + j * TPL * ROW, 0, kStreamPolicy);
-#pragma unroll
-      for (int j = 0; j < VL; ++j)
-        vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, v_off + j * TPL * ROW, 0, kStreamPolicy);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
-    auto consume = [&](const u32x4 *kb, const u32x4 *vb, int k) {
-      const int tc = w0 + (wave + NW * k) * kChunk;
-      const bool diag = tc + kChunk - 1 > pos0;   // some (token, row) pair is masked
-#pragma unroll
-      for (int j = 0; j < VL; ++j)
-        *reinterpret_cast<u32x4 *>(ktile + (v_row + j * TPL) * PITCH + 16 * v_col) = kb[j];
-      u32x4 ka[KI];
-#pragma unroll
-      for (int i = 0; i < KI; ++i)
-        ka[i] = *reinterpret_cast<const u32x4 *>(ktile + c16 * PITCH + 64 * i + 16 * g4);
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < KI; ++i) sacc = mfma_k32<DT>(ka[i], qf[i], sacc);
-      float sc[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * a.scale_log2;
-      u32x4 vr[VL];
-#pragma unroll
-      for (int j = 0; j < VL; ++j) vr[j] = vb[j];
-      if (diag) {
-        // Causal mask by select; V rows past the tile's last position are
-        // zeroed (whatever those slots hold must not meet a zero weight).
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (tc + 4 * g4 + r > cpos) sc[r] = kNegInf;
-#pragma unroll
-        for (int j = 0; j < VL; ++j)
-          if (tc + v_row + j * TPL >= t1) vr[j] = u32x4{0u, 0u, 0u, 0u};
+      for (int jj = 0; jj < LPW; ++jj) {
+        const int j = wave * LPW + jj;                   // 1 KB load index within the chunk
+        const int trow0 = tc + j * RPL;                  // first token of the load
+        const bool any = trow0 < wend;
+        const int phys =
+            __builtin_amdgcn_readfirstlane(any ? s_tbl[(trow0 - w0) >> a.log2_block] : 0);
+        const int off = trow0 & (a.block_size - 1);
+        const size_t base = ((size_t)phys * block_stride + (size_t)off * D) * E;
+        const int range = any ? RPL * ROW : 0;
+        const int row = dma_row;
+        const int voff = (trow0 + row < wend)
+                             ? row * ROW + ((dma_pp ^ ((j * RPL + row) % PIECES)) << 4)
+                             : 0x7ffffff0;
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(kbase + base), (short)0, range, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(vbase + base), (short)0, range, kBufferFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kr, (__attribute__((address_space(3))) void *)(sk + j * 1024), 16, voff, 0, 0,
+            kStreamPolicy);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (__attribute__((address_space(3))) void *)(sv + j * 1024), 16, voff, 0, 0,
+            kStreamPolicy);
       }
-#pragma unroll
-      for (int j = 0; j < VL; ++j)
-        *reinterpret_cast<u32x4 *>(tile_v + (v_row + j * TPL) * PITCH + 16 * v_col) = vr[j];
+    };
 
-      const float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    auto compute = [&](int k, const unsigned char *sk, const unsigned char *sv) {
+      const int tc = w0 + k * kCh;
+      if (wrows == 0 || tc > wlast) return;      // uniform: the chunk is after this wave's rows
+      const bool diag = tc + kCh - 1 > wpos0;
+      float sc[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          const u32x4 ka = *reinterpret_cast<const u32x4 *>(sk + k_addr(tt, i));
+          acc = mfma_k32<DT>(ka, qf[i], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[tt][r] = acc[r] * a.scale_log2;
+      }
+      if (diag) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (tc + 16 * tt + 4 * g4 + r > cpos) sc[tt][r] = kNegInf;
+      }
+      float mloc = sc[0][0];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[tt][r]);
       if (__builtin_amdgcn_ballot_w64(mloc > m + kLazyMax)) {
         const float cm = max_xor32(max_xor16(mloc));
         const float mnew = fmaxf(m, cm);
@@ -214,84 +261,71 @@ void prefill_kernel(PrefillArgs a) {
         m = mnew;
       }
       const float msafe = m == kNegInf ? 0.f : m;
-      float pw[4];
+      float p[2][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pw[r] = exp2_fast(sc[r] - msafe);
-        l += pw[r];
-      }
-      uint32_t h01, l01, h23, l23;
-      split2<DT>(pw[0], pw[1], h01, l01);
-      split2<DT>(pw[2], pw[3], h23, l23);
-      const u32x2 phi = {h01, h23}, plo = {l01, l23};
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[tt][r] = exp2_fast(sc[tt][r] - msafe);
+          l += p[tt][r];
+        }
+      const u32x4 pa_hi = {pack_p<DT>(p[0][0], p[0][1]), pack_p<DT>(p[0][2], p[0][3]),
+                           pack_p<DT>(p[1][0], p[1][1]), pack_p<DT>(p[1][2], p[1][3])};
+      u32x4 pa_lo = {0u, 0u, 0u, 0u};
+      if constexpr (DT == kBF16)
+        pa_lo = u32x4{pack_lo_bf16(p[0][0], p[0][1]), pack_lo_bf16(p[0][2], p[0][3]),
+                      pack_lo_bf16(p[1][0], p[1][1]), pack_lo_bf16(p[1][2], p[1][3])};
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(tr_base + 32 * n));
-        const u32x2 vf = __builtin_bit_cast(u32x2, t);
-        o[n] = mfma_k16<DT>(phi, vf, o[n]);
-        o[n] = mfma_k16<DT>(plo, vf, o[n]);
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(sv + v_addr(0, n)));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(sv + v_addr(1, n)));
+        const u32x2 w0v = __builtin_bit_cast(u32x2, v0), w1v = __builtin_bit_cast(u32x2, v1);
+        const u32x4 vf = {w0v.x, w0v.y, w1v.x, w1v.y};
+        o[n] = mfma_k32<DT>(pa_hi, vf, o[n]);
+        if constexpr (DT == kBF16) o[n] = mfma_k32<DT>(pa_lo, vf, o[n]);
       }
     };
 
-    constexpr int NBUF = 2;
-    u32x4 kb[NBUF][VL], vb[NBUF][VL];
-    if (nch_w > 0) {
-      const int last = nch_w - 1;
-      load(kb[0], vb[0], 0, last);
-      for (int k0 = 0; k0 < nch_w; k0 += NBUF) {
-#pragma unroll
-        for (int i = 0; i < NBUF; ++i) {
-          const int k = k0 + i;
-          if (k >= nch_w) break;
-          load(kb[(i + 1) % NBUF], vb[(i + 1) % NBUF], k + 1, last);
-          consume(kb[i], vb[i], k);
-        }
-      }
+    dma(0, s_k0, s_v0);
+    for (int k = 0; k < nch; k += 2) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);       // this wave's part of chunk k has landed
+      __syncthreads();                                // chunk k is in stage 0 for every wave
+      if (k + 1 < nch) dma(k + 1, s_k1, s_v1);
+      compute(k, s_k0, s_v0);
+      if (k + 1 >= nch) break;
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();                                // chunk k+1 in stage 1; stage 0 is free
+      if (k + 2 < nch) dma(k + 2, s_k0, s_v0);
+      compute(k + 1, s_k1, s_v1);
     }
   }
 
   if (poison) {
-    for (int idx = tid; idx < nrows * D; idx += NW * 64) {
+    for (int idx = tid; idx < nrows * D; idx += kPfWaves * 64) {
       const int r = idx / D, d = idx - r * D;
       store_out<DT>(a.out, ((size_t)(q0 + r0 + r) * H + h) * D + d, &nan, 1);
     }
     return;
   }
+  if (wrows == 0) return;
 
+  // Row sums over the four lane groups, then out = O / l for each row this
+  // lane holds (rows 4*g4 + r of the wave, dims 16n + c16).
   l = sum_xor32(sum_xor16(l));
-  __syncthreads();
-  float *s_m = reinterpret_cast<float *>(s_buf);                // [NW][kRows]
-  float *s_l = s_m + NW * kRows;                                 // [NW][kRows]
-  float *s_o = s_l + NW * kRows;                                 // [NW][kRows][D]
-  if (g4 == 0) {
-    s_m[wave * kRows + c16] = m;
-    s_l[wave * kRows + c16] = l;
-  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int q = 4 * g4 + r;
-    if (q < nrows) {
+    const float lr = __shfl(l, q);
+    if (q < wrows) {
+      const size_t rowbase = ((size_t)(q0 + r0 + wr0 + q) * H + h) * D;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) s_o[(wave * kRows + q) * D + 16 * n + c16] = o[n][r];
+      for (int n = 0; n < NT; ++n) {
+        const float v = lr == 0.f ? 0.f : o[n][r] / lr;
+        store_out<DT>(a.out, rowbase + 16 * n + c16, &v, 1);
+      }
     }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < nrows * D; idx += NW * 64) {
-    const int q = idx / D, d = idx - q * D;
-    float Mw = s_m[q];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) Mw = fmaxf(Mw, s_m[w * kRows + q]);
-    const float Ms = Mw == kNegInf ? 0.f : Mw;
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = exp2_fast(s_m[w * kRows + q] - Ms);
-      L += f * s_l[w * kRows + q];
-      O += f * s_o[(w * kRows + q) * D + d];
-    }
-    const float r = L == 0.f ? 0.f : O / L;
-    store_out<DT>(a.out, ((size_t)(q0 + r0 + q) * H + h) * D + d, &r, 1);
   }
 }
 
@@ -299,8 +333,8 @@ template <int DT, int D>
 hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   const long n = (long)a.num_seqs * a.num_heads * a.num_tiles;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<DT, D, kGqaWaves>), dim3((unsigned)n), dim3(kGqaWaves * 64),
-                     0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<DT, D>), dim3((unsigned)n), dim3(kPfWaves * 64), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
