@@ -4,7 +4,7 @@
 
 Every HIP source is compiled with -O3 for gfx950 only, with the packed-fp32
 instruction feature switched off (``-Xclang -target-feature -Xclang
--packed-fp32-ops``); the library is linked against the HIP runtime by soname
+-packed-fp32-ops``) and matrix-core accumulators kept in VGPRs; the library is linked against the HIP runtime by soname
 (libamdhip64.so.7), which is the copy PyTorch has already loaded when the
 Python binding opens it.
 """
@@ -28,7 +28,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
-DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# -amdgpu-mfma-vgpr-form: matrix-core accumulators live in ordinary VGPRs
+# (gfx950 allows either); with AGPR accumulators the compiler copied all of
+# them between register files on every chunk of the prefill loop.
+DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str) -> str:
