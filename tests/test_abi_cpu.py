@@ -103,3 +103,76 @@ def test_partition_and_workspace_sizes(lib):
         P = pa.pa_decode_partition_size(S, H, Hkv, 128, B, ctx, 0, torch.bfloat16)
         assert 256 <= P <= 4096 and P % B == 0
     assert pa.pa_decode_partition_size(1, 3, 2, 128, 16, 10, 0, torch.float16) == -1
+
+
+FP8 = 3
+
+
+def test_decode_fp8_rejects(lib):
+    def call(**kw):
+        a = dict(out=_p(), q=_p(), k=_p(), v=_p(), bt=_p(), cl=_p(), S=2, H=8, Hkv=8, D=128, B=16,
+                 NB=64, MB=8, maxctx=128, scale=0.1, ks=0.5, vs=0.5, P=0, ws=None, wsb=0, dt=F16)
+        a.update(kw)
+        return lib.pa_decode_fp8(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["H"],
+                                 a["Hkv"], a["D"], a["B"], a["NB"], a["MB"], a["maxctx"], a["scale"],
+                                 a["ks"], a["vs"], a["P"], a["ws"], a["wsb"], a["dt"], None)
+    assert call(dt=F32) == _capi.PA_ERR_UNSUPPORTED          # fp16/bf16 queries only
+    assert call(dt=FP8) == _capi.PA_ERR_UNSUPPORTED
+    assert call(ks=0.0) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(vs=float("nan")) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(H=8, Hkv=3) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(q=None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(S=0, q=None, out=None) == _capi.PA_OK
+    # pa_decode refuses E4M3 pools (they go through pa_decode_fp8)
+    assert _decode(lib, dt=FP8) == _capi.PA_ERR_UNSUPPORTED
+    # sizing with the E4M3 pool type follows the vector kernel's work items
+    assert lib.pa_decode_partition_size(16, 64, 8, 128, 16, 4096, 0, FP8) >= 256
+    assert lib.pa_decode_workspace_size(8, 32, 32, 128, 64, 32768, 512, FP8) == \
+        lib.pa_decode_workspace_size(8, 32, 32, 128, 64, 32768, 512, F16)
+
+
+def test_cache_write_fp8_rejects(lib):
+    cw = lib.pa_cache_write_fp8
+    ok = (_p(), _p(), _p(), _p(), _p(), 4, 8, 128, 16, 64)
+    assert cw(*ok, FP8, 1.0, 1.0, None) == _capi.PA_ERR_UNSUPPORTED     # source must be f32/f16/bf16
+    assert cw(_p(), _p(), _p(), _p(), _p(), 4, 8, 72, 16, 64, F16, 1.0, 1.0, None) == \
+        _capi.PA_ERR_UNSUPPORTED                                           # head_dim % 16
+    assert cw(*ok, F16, -1.0, 1.0, None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert cw(*ok, F16, 1.0, float("inf"), None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert cw(_p(), _p(), _p(), _p(), None, 4, 8, 128, 16, 64, F16, 1.0, 1.0, None) == \
+        _capi.PA_ERR_INVALID_ARGUMENT
+    assert cw(_p(8), _p(), _p(), _p(), _p(), 4, 8, 128, 16, 64, F16, 1.0, 1.0, None) == \
+        _capi.PA_ERR_INVALID_ARGUMENT                                      # misaligned
+    assert cw(None, None, None, None, None, 0, 8, 128, 16, 64, F16, 1.0, 1.0, None) == _capi.PA_OK
+
+
+def test_prefill_rejects(lib):
+    def call(**kw):
+        a = dict(out=_p(), q=_p(), k=_p(), v=_p(), bt=_p(), cl=_p(), qs=_p(), S=2, T=40, H=8,
+                 Hkv=8, D=128, B=16, NB=64, MB=8, mq=32, maxctx=128, scale=0.1, dt=F16)
+        a.update(kw)
+        return lib.pa_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["S"],
+                              a["T"], a["H"], a["Hkv"], a["D"], a["B"], a["NB"], a["MB"], a["mq"],
+                              a["maxctx"], a["scale"], a["dt"], None)
+    assert call(dt=F32) == _capi.PA_ERR_UNSUPPORTED
+    assert call(D=96) == _capi.PA_ERR_UNSUPPORTED
+    assert call(H=6, Hkv=4) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(mq=200) == _capi.PA_ERR_INVALID_ARGUMENT                  # > max_context_len
+    assert call(maxctx=200) == _capi.PA_ERR_INVALID_ARGUMENT              # > MB * B
+    assert call(T=-1) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(qs=None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(q=_p(260)) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(scale=float("nan")) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(T=0, q=None, out=None) == _capi.PA_OK
+    assert call(mq=0, q=None, out=None) == _capi.PA_OK
+
+
+def test_copy_blocks_rejects(lib):
+    cb = lib.pa_copy_blocks
+    assert cb(_p(), None, _p(), None, _p(), -1, 4096, 8, 8, None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert cb(_p(), None, _p(), None, _p(), 2, 4000, 8, 8, None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert cb(_p(), None, _p(), None, _p(), 2, 4096, 0, 8, None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert cb(_p(), _p(), _p(), None, _p(), 2, 4096, 8, 8, None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert cb(None, None, _p(), None, _p(), 2, 4096, 8, 8, None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert cb(_p(8), None, _p(), None, _p(), 2, 4096, 8, 8, None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert cb(None, None, None, None, None, 0, 4096, 8, 8, None) == _capi.PA_OK
