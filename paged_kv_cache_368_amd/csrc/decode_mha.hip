@@ -190,10 +190,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
         store_out<DT>(a.out, row_out + tid, &v, 1);
       }
     } else {
-      if (tid < D) a.ws_o[part * D + tid] = nan;
+      if (tid < D) store_partial(a.ws_o + part * D + tid, nan);
       if (tid == 0) {
-        a.ws_ml[2 * part] = __builtin_inff();
-        a.ws_ml[2 * part + 1] = nan;
+        store_partial(a.ws_ml + 2 * part, __builtin_inff());
+        store_partial(a.ws_ml + 2 * part + 1, nan);
       }
     }
     return;
@@ -347,10 +347,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
       const float r = L == 0.f ? 0.f : O / L;   // NaN (a poisoned partition) propagates
       store_out<DT>(a.out, row_out + tid, &r, 1);
     } else {
-      a.ws_o[part * D + tid] = O;
+      store_partial(a.ws_o + part * D + tid, O);
       if (tid == 0) {
-        a.ws_ml[2 * part] = Mw;
-        a.ws_ml[2 * part + 1] = L;
+        store_partial(a.ws_ml + 2 * part, Mw);
+        store_partial(a.ws_ml + 2 * part + 1, L);
       }
     }
   }

@@ -81,6 +81,16 @@ __device__ __forceinline__ void store_out(void *base, size_t elem, const float *
   }
 }
 
+// Split-context partial states of the vector kernel (read once, by the merge
+// launch that follows): written through to memory with agent-scope stores
+// rather than left dirty in the XCD's L2.  Measured on a 32k-token, 64-way
+// split: 2.7% less time per call than plain stores; on the grouped-query
+// kernel's few, larger partials plain stores were 1.5% faster, so that
+// kernel keeps them.
+__device__ __forceinline__ void store_partial(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- cross-lane ------------------------------------------------------------
 
 // DPP controls (gfx9 encoding).

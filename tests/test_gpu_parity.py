@@ -298,3 +298,35 @@ def test_decode_grouped_query_scores_spread_wide():
     for ps in (0, 64):
         got = _run_decode(wl, ps)
         _assert_close(got, ref, "bf16", f"gqa wide P={ps}")
+
+
+@pytest.mark.parametrize("dtype,H,Hkv", [("bf16", 16, 2), ("f16", 4, 4), ("f32", 4, 2)])
+def test_decode_split_ignores_workspace_contents(dtype, H, Hkv):
+    """Split contexts go through the caller's workspace (fp32 partials, then
+    the merge pass).  All-ones, random and stale workspace bytes must give
+    bit-identical outputs on calls in a row with one workspace."""
+    wl = build("ws", dtype, [300, 1000, 77, 2048, 16], H, Hkv, 128, 16, seed=61, pool="choice",
+               pool_factor=1.2)
+    ref = _oracle(wl)
+    dev = to_device(wl)
+    S = wl.num_seqs
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for ps in (16, 256):
+        n = pa.pa_decode_workspace_size(S, H, Hkv, 128, 16, wl.max_context_len, ps, dev.q.dtype)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        first = None
+        for fill in ("ones", "random", "stale", "stale"):
+            _say(f"split workspace {dtype} H={H}/{Hkv} P={ps} {fill}")
+            if fill == "ones":
+                ws.fill_(255)
+            elif fill == "random":
+                ws.copy_(torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=gen))
+            dev.out.fill_(float("nan"))
+            pa.pa_decode(dev.out, dev.q, dev.key_cache, dev.value_cache, dev.block_tables,
+                         dev.context_lens, wl.max_context_len, wl.scale, ps, workspace=ws)
+            torch.cuda.synchronize()
+            got = P.to_f64(from_torch(dev.out, dtype), dtype)
+            _assert_close(got, ref, dtype, f"workspace {fill} P={ps}")
+            if first is None:
+                first = got
+            assert np.array_equal(got, first), f"{fill}: output differs from the first call"
