@@ -1,9 +1,12 @@
 """Decode-step benchmark on one MI355X.
 
 One step = the whole decode hot path for one batch: the slot of each
-sequence's newest token (pa_compute_slots), the write of its K/V into the
-pool (pa_cache_write), and paged attention over every context token
-(pa_decode, with its log-sum-exp merge pass when partitions split a context).
+sequence's newest token, the write of its K/V into the pool, and paged
+attention over every context token.  By default the step is one call of
+pa_append_decode, which does all three in one launch (plus the log-sum-exp
+merge launch when partitions split a context); ``--step three`` times the
+same step as pa_compute_slots + pa_cache_write + pa_decode (always so for
+fp8 pools).
 
 Prints ONE JSON line.  ``value`` is context tokens per second (sum of
 context_lens over a step / step time) with every input already in HBM.
@@ -56,19 +59,24 @@ COUNTERS = {
 
 
 def algorithmic_bytes(context_lens, num_heads, num_kv_heads, head_dim, block_size, dtype,
-                      kv_dtype=None) -> dict:
+                      kv_dtype=None, new_row_write=False) -> dict:
     """Bytes a decode launch must move at minimum: K and V rows of every
     context token (per kv head), q and out (per query head) and the 4-byte
     table entries in use.  Per token per kv head K+V is 2*D*e bytes, the
     per-layer form of the KV size formula (2 x tokens x heads x head_dim x
-    element bytes)."""
+    element bytes).  ``new_row_write``: the launch also stores the newest
+    token's K and V rows into the pool (pa_append_decode), 2*D*e bytes per
+    sequence and kv head (that token's rows are read from the input instead
+    of the pool, the same bytes)."""
     e = ELEM[dtype]
     ekv = ELEM[kv_dtype or dtype]
     ctx = [int(c) for c in context_lens]
     kv = sum(ctx) * num_kv_heads * head_dim * ekv * 2
     qo = 2 * len(ctx) * num_heads * head_dim * e
     table = sum(-(-c // block_size) for c in ctx) * 4
-    return {"kv": kv, "q_out": qo, "table": table, "total": kv + qo + table}
+    write = sum(1 for c in ctx if c > 0) * num_kv_heads * head_dim * ekv * 2 if new_row_write else 0
+    return {"kv": kv, "q_out": qo, "table": table, "kv_write": write,
+            "total": kv + qo + table + write}
 
 
 def kernel_source_digest() -> str:
@@ -86,10 +94,11 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, block_size: int, partition_size: int):
-    """HBM bytes per pa_decode call from the stored counters, or None when
-    none were taken for this workload on the current kernel sources."""
-    c = COUNTERS.get(f"{workload}/B{block_size}/P{partition_size}")
+def measured_traffic(workload: str, block_size: int, partition_size: int, fused: bool = False):
+    """HBM bytes per decode call (pa_append_decode when ``fused``, else
+    pa_decode) from the stored counters, or None when none were taken for
+    this workload on the current kernel sources."""
+    c = COUNTERS.get(f"{workload}/B{block_size}/P{partition_size}" + ("/append" if fused else ""))
     if c is None or c["sources"] != kernel_source_digest():
         return None
     return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024
@@ -371,6 +380,9 @@ def main(argv=None) -> int:
     ap.add_argument("--prefix", type=int, default=0,
                     help="--op prefill: tokens of each 2048-token prompt already cached")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs for --op copy_blocks")
+    ap.add_argument("--step", choices=["fused", "three"], default="fused",
+                    help="decode step as one pa_append_decode call (default) or as "
+                         "pa_compute_slots + pa_cache_write + pa_decode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     args = ap.parse_args(argv)
@@ -407,7 +419,9 @@ def main(argv=None) -> int:
     lib = pa.load_library()
     P_used = lib.pa_decode_partition_size(S, H, Hkv, D, B, maxctx, wl.partition_size, size_dt)
     ws_bytes = lib.pa_decode_workspace_size(S, H, Hkv, D, B, maxctx, wl.partition_size, size_dt)
-    nbytes = algorithmic_bytes(wl.context_lens, H, Hkv, D, B, dt, wl.pool_dtype)
+    fused = args.step == "fused" and not fp8
+    nbytes = algorithmic_bytes(wl.context_lens, H, Hkv, D, B, dt, wl.pool_dtype,
+                               new_row_write=fused)
     sum_ctx = int(wl.context_lens.sum())
 
     base = to_device(wl)
@@ -426,6 +440,15 @@ def main(argv=None) -> int:
 
     def step(i, ev=None):
         kc, vc = pools[i % copies]
+        if fused:
+            if ev is not None:
+                ev[0].record(stream)
+            pa.pa_append_decode(base.out, base.q, base.new_key, base.new_value, kc, vc,
+                                base.block_tables, base.context_lens, maxctx, wl.scale,
+                                wl.partition_size, workspace)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         pa.pa_compute_slots(slots, base.block_tables, B, wl.num_blocks, context_lens=base.context_lens)
         if fp8:
             pa.pa_cache_write_fp8(base.new_key, base.new_value, kc, vc, slots, wl.k_scale,
@@ -489,11 +512,15 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": B, "sum_context_tokens": sum_ctx,
                    "max_context_len": maxctx, "partition_size": P_used, "seed": wl.seed,
-                   "pool_copies_rotated": copies},
+                   "pool_copies_rotated": copies,
+                   "step": ("pa_append_decode: slot, K/V write and attention in one launch"
+                            if fused else "pa_compute_slots + pa_cache_write(_fp8) + "
+                            "pa_decode(_fp8)")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(wl.name, B, P_used),
-                     "kernel": "pa_decode (decode kernel + merge pass when split)",
+                     "traffic": measured_traffic(wl.name, B, P_used, fused),
+                     "kernel": ("pa_append_decode" if fused else "pa_decode") +
+                               " (decode kernel + merge pass when split)",
                      "bytes_per_launch": nbytes["total"], "mean_launch_us": dec_mean_s * 1e6,
                      "median_launch_us": dec_med_s * 1e6},
         "decode_context_tokens_per_s": sum_ctx / dec_mean_s,

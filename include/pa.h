@@ -179,6 +179,40 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
                       pa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * pa_append_decode -- one decode step in one launch: for every sequence s
+ * with context_lens[s] >= 1, token t = context_lens[s] - 1 is the newest
+ * one.  Its K/V rows (key[s], value[s]) are written to its slot
+ * block_tables[s][t / block_size] * block_size + t % block_size (the cache
+ * write of P2 §2.1 and P3 §3, with the slot resolved as pa_compute_slots
+ * does), and out[s] is pa_decode's result over tokens 0..t, the newest
+ * token's K/V taken from key/value.  Outputs and the pools afterwards are
+ * bit-identical to pa_compute_slots + pa_cache_write + pa_decode on the same
+ * inputs.
+ *
+ *   key, value     in   [num_seqs][num_kv_heads][head_dim], storage type
+ *                       dtype, 16-byte aligned: the newest token's rows
+ *   key_cache, value_cache  in/out  the pools, as for pa_decode
+ *   every other argument as for pa_decode.
+ *
+ * Sequences with context_lens[s] == 0 write nothing and get zeros.  Outputs
+ * are poisoned (NaN) exactly as pa_decode's.  The newest token's rows are
+ * written whenever its context length is one pa_decode accepts and its own
+ * block id lies inside the pool (a bad id elsewhere in the table poisons the
+ * output but does not stop the write, as with pa_cache_write).  The slot of the
+ * newest token must not be shared with another sequence's context (copy a
+ * shared last block first, pa_copy_blocks).  dtype PA_F32, PA_F16 or PA_BF16
+ * (E4M3 pools: pa_cache_write_fp8, then pa_decode_fp8).
+ */
+pa_status_t pa_append_decode(void *out, const void *q, const void *key, const void *value,
+                             void *key_cache, void *value_cache, const int32_t *block_tables,
+                             const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t max_context_len, float scale, int32_t partition_size,
+                             void *workspace, size_t workspace_bytes, pa_dtype_t dtype,
+                             hipStream_t stream);
+
+/*
  * pa_prefill -- paged attention for many query tokens per sequence (a prompt,
  * or the new part of a prompt whose prefix is already cached), on the matrix
  * cores.  The pages give the per-token step (P2 §2.1: the token's K/V join

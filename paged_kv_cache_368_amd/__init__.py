@@ -15,6 +15,7 @@ from ._capi import (  # noqa: F401
     pa_cache_write_fp8,
     pa_copy_blocks,
     pa_compute_slots,
+    pa_append_decode,
     pa_decode,
     pa_decode_fp8,
     pa_decode_partition_size,

@@ -55,6 +55,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, i32, i32, i32,
                               c.c_float, i32, ptr, sz, c.c_int, ptr]
     lib.pa_decode.restype = st
+    lib.pa_append_decode.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32,
+                                     i32, i32, i32, i32, c.c_float, i32, ptr, sz, c.c_int, ptr]
+    lib.pa_append_decode.restype = st
     f32 = c.c_float
     lib.pa_cache_write_fp8.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, c.c_int,
                                        f32, f32, ptr]
@@ -331,6 +334,50 @@ def pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, block_
     return load_library().pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim,
                                                    block_size, max_context_len, partition_size,
                                                    DTYPE_CODES[dtype])
+
+
+def pa_append_decode(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                     key_cache: torch.Tensor, value_cache: torch.Tensor,
+                     block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                     scale: float | None = None, partition_size: int = 0,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step in one launch: writes each sequence's newest token
+    (position context_lens - 1; rows ``key``/``value`` [S][Hkv][D]) into its
+    slot and runs decode into ``out``; see include/pa.h."""
+    lib = load_library()
+    for n, t in (("out", out), ("q", q), ("key", key), ("value", value),
+                 ("key_cache", key_cache), ("value_cache", value_cache),
+                 ("block_tables", block_tables), ("context_lens", context_lens)):
+        _dev(t, n)
+    if q.dtype not in DTYPE_CODES or any(t.dtype != q.dtype
+                                         for t in (out, key, value, key_cache, value_cache)):
+        raise ValueError("q, out, key, value and the pools must share one of "
+                         "float32/float16/bfloat16")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    S, H, D = q.shape
+    NB, Hkv, B, D2 = key_cache.shape
+    if D2 != D or tuple(value_cache.shape) != (NB, Hkv, B, D) or tuple(out.shape) != (S, H, D):
+        raise ValueError("shape mismatch between q, out and the pools")
+    if tuple(key.shape) != (S, Hkv, D) or tuple(value.shape) != (S, Hkv, D):
+        raise ValueError("key and value must be [num_seqs][num_kv_heads][head_dim]")
+    if block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables and context_lens must have one row per sequence")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = pa_decode_workspace_size(S, H, Hkv, D, B, max_context_len, partition_size, q.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_append_decode(
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(key.data_ptr()), ctypes.c_void_p(value.data_ptr()),
+        ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(context_lens.data_ptr()),
+        S, H, Hkv, D, B, NB, block_tables.shape[1], max_context_len, float(scale),
+        partition_size, ws_ptr, ws_bytes, DTYPE_CODES[q.dtype], _stream(q)))
+    return out
 
 
 def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,

@@ -35,6 +35,11 @@
 // to output-row lanes) is rare; unnormalised weights stay below 2^8, far
 // from fp32 or bf16 limits, and the final o/l is independent of the
 // reference chosen.
+//
+// Appending decode: as on the vector kernel, the newest token's K/V rows come
+// from the input (the pool is streamed only up to the token before it, and
+// the new row is taken as one extra masked chunk after the loop) and the
+// work-group of the partition holding it stores them into its slot.
 #include "pa_mfma.h"
 
 namespace pa {
@@ -61,6 +66,7 @@ void decode_gqa_kernel(DecodeArgs a) {
   constexpr int VL = kChunk / TPL;           // V loads per chunk
 
   __shared__ int s_tbl[kMaxPartBlocks];
+  __shared__ u32x4 s_new[2][ROW / 16];      // the newest token's K and V rows (appending)
   // K and V tiles (one pair per wave) during the loop; reused for the
   // cross-wave merge afterwards.
   constexpr int kTileBytes = kChunk * PITCH;
@@ -91,6 +97,20 @@ void decode_gqa_kernel(DecodeArgs a) {
   const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks_per_seq + b0;
   const int window = min(P >> a.log2_block, a.max_blocks_per_seq - b0);
   const int id = tid < window ? trow[tid] : -1;
+  // K and V: contiguous wave loads (every load instruction reads whole 1 KB
+  // of the chunk), lane l reads row (l/LPT) + TPL*j, bytes 16*(l%LPT).
+  const int v_row = lane / LPT, v_col = lane % LPT;
+  const bool append = a.new_k != nullptr;                  // uniform (kernel argument)
+  // Lanes 0..LPT-1 (wave 0, row 0) hold the newest token's rows.
+  const bool new_lane = append && tid < LPT;
+  u32x4 nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
+  if (new_lane) {
+    const size_t new_off = ((size_t)s * Hkv + kvh) * ROW + 16 * v_col;
+    nk = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.new_k) + new_off);
+    nv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.new_v) + new_off);
+    s_new[0][v_col] = nk;
+    s_new[1][v_col] = nv;
+  }
   u32x4 qf[KI];
   {
     const bool live = c16 < G;
@@ -114,6 +134,22 @@ void decode_gqa_kernel(DecodeArgs a) {
   if (tid < nblk) s_tbl[tid] = id;
   const bool poison = __syncthreads_or(bad_id) || bad_ctx;
 
+  const size_t head_stride = (size_t)a.block_size * D;
+  const size_t block_stride = head_stride * Hkv;
+  // The new token's slot, written by the partition that holds the token.
+  // Like the separate cache write, it needs only the token's own slot to be
+  // valid (a bad id elsewhere in the table poisons the output, not the write).
+  if (new_lane && !bad_ctx && ctx > t0 && ctx <= t1) {
+    const int tn = ctx - 1;
+    const int phys = s_tbl[(tn - t0) >> a.log2_block];
+    if (phys >= 0 && phys < a.num_blocks) {
+      const size_t dst = ((size_t)phys * block_stride + kvh * head_stride +
+                          (size_t)(tn & (a.block_size - 1)) * D) * E + 16 * v_col;
+      *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_store) + dst) = nk;
+      *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_store) + dst) = nv;
+    }
+  }
+
   if (poison) {
     const float nan = __builtin_nanf("");
     for (int idx = tid; idx < G * D; idx += NW * 64) {
@@ -133,18 +169,17 @@ void decode_gqa_kernel(DecodeArgs a) {
     return;
   }
 
-  const int nch = (t1 - t0 + kChunk - 1) / kChunk;
+  // Tokens read from the pool: [t0, tp); the newest token, when appending,
+  // comes from LDS instead.
+  const bool holds_new = append && ctx > t0 && ctx <= t1;        // uniform
+  const int tp = holds_new ? ctx - 1 : t1;
+  const int nch = (tp - t0 + kChunk - 1) / kChunk;
   const int nch_w = nch > wave ? (nch - wave + NW - 1) / NW : 0;
   int my_ids = 0;
   if (lane < nch_w) my_ids = s_tbl[((wave + NW * lane) * kChunk) >> a.log2_block];
 
-  const size_t head_stride = (size_t)a.block_size * D;
-  const size_t block_stride = head_stride * Hkv;
   const char *kbase = reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E;
   const char *vbase = reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E;
-  // K and V: contiguous wave loads (every load instruction reads whole 1 KB
-  // of the chunk), lane l reads row (l/LPT) + TPL*j, bytes 16*(l%LPT).
-  const int v_row = lane / LPT, v_col = lane % LPT;
   const int v_off = v_row * ROW + 16 * v_col;
   constexpr int kChunkBytes = kChunk * ROW;
 
@@ -186,9 +221,9 @@ void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
   for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto consume = [&](const u32x4 *kb, const u32x4 *vb, int k) {
-    const int tc = t0 + (wave + NW * k) * kChunk;
-    const bool tail = tc + kChunk > t1;                  // wave-uniform
+  // One 16-token chunk starting at token tc; rows at or past tend are masked.
+  auto consume = [&](const u32x4 *kb, const u32x4 *vb, int tc, int tend) {
+    const bool tail = tc + kChunk > tend;                // wave-uniform
     // K: through this wave's LDS tile into the A layout (lane l: token l%16,
     // bytes 64i + 16*(l/16) of its row).  Rows past the context are left as
     // they are: their scores are replaced by -inf below, by select.
@@ -214,10 +249,10 @@ void decode_gqa_kernel(DecodeArgs a) {
       // holds must not meet a zero weight as NaN).
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (tc + 4 * g4 + r >= t1) sc[r] = kNegInf;
+        if (tc + 4 * g4 + r >= tend) sc[r] = kNegInf;
 #pragma unroll
       for (int j = 0; j < VL; ++j)
-        if (tc + v_row + j * TPL >= t1) vr[j] = u32x4{0u, 0u, 0u, 0u};
+        if (tc + v_row + j * TPL >= tend) vr[j] = u32x4{0u, 0u, 0u, 0u};
     }
     // V: stage the chunk in this wave's LDS tile.
 #pragma unroll
@@ -275,9 +310,20 @@ void decode_gqa_kernel(DecodeArgs a) {
         const int k = k0 + i;
         if (k >= nch_w) break;
         load(kb[(i + 1) % NBUF], vb[(i + 1) % NBUF], k + 1, last);
-        consume(kb[i], vb[i], k);
+        consume(kb[i], vb[i], t0 + (wave + NW * k) * kChunk, tp);
       }
     }
+  }
+  // The newest token as a chunk of one valid row (row 0, on wave 0).
+  if (holds_new && wave == 0) {
+    u32x4 kn[VL], vn[VL];
+#pragma unroll
+    for (int j = 0; j < VL; ++j) {
+      const bool mine = j == 0 && v_row == 0;
+      kn[j] = mine ? s_new[0][v_col] : u32x4{0u, 0u, 0u, 0u};
+      vn[j] = mine ? s_new[1][v_col] : u32x4{0u, 0u, 0u, 0u};
+    }
+    consume(kn, vn, ctx - 1, ctx);
   }
 
   // Column sums over the four lane groups.

@@ -31,6 +31,15 @@
 // Masking.  Tokens past the context in the last chunk get score -inf and
 // their V words are zeroed by select, so whatever the unused slots hold
 // (NaN in the tests) never reaches the result.
+//
+// Appending decode (pa_append_decode, pools of the query's type): the newest
+// token of each sequence (position context_lens - 1) arrives as an input row.
+// The row is loaded with q and kept in LDS; the partition that holds the
+// token streams the pool only up to the token before it (whatever the slot
+// held before never counts) and takes the new row as one extra masked chunk
+// after its loop, and one work-group per (sequence, kv head) stores it into
+// the slot for later steps: the slot resolution, the cache write and the
+// attention of a decode step in one launch.
 #include "pa_device.h"
 
 namespace pa {
@@ -131,6 +140,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   __shared__ int s_tbl[kMaxPartBlocks];
   __shared__ float s_o[NW][D];
   __shared__ float s_m[NW], s_l[NW];
+  __shared__ u32x4 s_new[2][LPT];           // the newest token's K and V rows (appending)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -167,6 +177,18 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   for (int i = 0; i < QW; ++i)
     qv[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.q) +
                                              (row_out + col * EPL) * EQ + 16 * i);
+  constexpr bool kCanAppend = KT != kFP8;
+  const bool append = kCanAppend && a.new_k != nullptr;        // uniform (kernel argument)
+  // Lanes 0..LPT-1 (wave 0, row 0) hold the newest token's rows.
+  const bool new_lane = append && tid < LPT;
+  u32x4 nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
+  if (new_lane) {
+    const size_t new_off = (((size_t)s * a.num_kv_heads + kvh) * D + col * EPL) * E;
+    nk = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.new_k) + new_off);
+    nv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.new_v) + new_off);
+    s_new[0][col] = nk;
+    s_new[1][col] = nv;
+  }
 
   const bool bad_ctx = ctx < 0 || ctx > a.max_context_len ||
                        ctx > a.max_blocks_per_seq * a.block_size;
@@ -182,6 +204,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   const bool poison = __syncthreads_or(bad_id) || bad_ctx;
 
   const size_t part = ((size_t)s * H + h) * a.num_partitions + p;
+  // The new token's slot: written by the first query head of its kv head, in
+  // the partition that holds the token (one 16-byte slice per lane of row 0).
+  const size_t head_stride = (size_t)a.block_size * D;        // elements per (block, head) tile
+  const size_t block_stride = head_stride * a.num_kv_heads;
+  // Like the separate cache write, it needs only the token's own slot to be
+  // valid (a bad id elsewhere in the table poisons the output, not the write).
+  if (new_lane && !bad_ctx && ctx > t0 && ctx <= t1 && h % G == 0) {
+    const int tn = ctx - 1;
+    const int phys = s_tbl[(tn - t0) >> a.log2_block];
+    if (phys >= 0 && phys < a.num_blocks) {
+      const size_t dst = ((size_t)phys * block_stride + kvh * head_stride +
+                          (size_t)(tn & (a.block_size - 1)) * D + col * EPL) * E;
+      *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_store) + dst) = nk;
+      *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_store) + dst) = nv;
+    }
+  }
   if (poison) {
     const float nan = __builtin_nanf("");
     if (direct) {
@@ -199,14 +237,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
     return;
   }
 
-  const int nch = (t1 - t0 + kChunk - 1) / kChunk;
+  // Tokens read from the pool: [t0, tp); the newest token, when appending,
+  // comes from LDS instead.
+  const bool holds_new = append && ctx > t0 && ctx <= t1;        // uniform
+  const int tp = holds_new ? ctx - 1 : t1;
+  const int nch = (tp - t0 + kChunk - 1) / kChunk;
   const int nch_w = nch > wave ? (nch - wave + NW - 1) / NW : 0;
   // This wave's chunk k is partition chunk wave + NW*k; lane k keeps its block id.
   int my_ids = 0;
   if (lane < nch_w) my_ids = s_tbl[((wave + NW * lane) * kChunk) >> a.log2_block];
 
-  const size_t head_stride = (size_t)a.block_size * D;        // elements per (block, head) tile
-  const size_t block_stride = head_stride * a.num_kv_heads;
   const char *kbase = reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E;
   const char *vbase = reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E;
   const int lane_off = (row * D + col * EPL) * E;
@@ -250,16 +290,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < EPL; ++i) o[i] = 0.f;
 
-  auto consume = [&](const u32x4 *kb, const u32x4 *vb, int k) {
-    const int tc = t0 + (wave + NW * k) * kChunk;
+  // One 16-token chunk starting at token tc; rows at or past tend are masked.
+  auto consume = [&](const u32x4 *kb, const u32x4 *vb, int tc, int tend) {
     float sc[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) sc[j] = group_sum<LPT>(lane_dot<DT, KT>(qv, kb[j])) * a.scale_log2;
-    const bool tail = tc + kChunk > t1;                       // last chunk: mask past the context
+    const bool tail = tc + kChunk > tend;                     // last chunk: mask past the context
     bool valid[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      valid[j] = !tail || (tc + j * TPL + row < t1);
+      valid[j] = !tail || (tc + j * TPL + row < tend);
       sc[j] = valid[j] ? sc[j] : kNegInf;
     }
     float mloc = sc[0];
@@ -297,8 +337,21 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
         const int k = k0 + i;
         if (k >= nch_w) break;
         load(kb[(i + NBUF - 1) % NBUF], vb[(i + NBUF - 1) % NBUF], k + NBUF - 1, last);
-        consume(kb[i], vb[i], k);
+        consume(kb[i], vb[i], t0 + (wave + NW * k) * kChunk, tp);
       }
+    }
+  }
+  if constexpr (kCanAppend) {
+    // The newest token as a chunk of one valid row (row 0 of wave 0).
+    if (holds_new && wave == 0) {
+      u32x4 kn[NL], vn[NL];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const bool mine = j == 0 && row == 0;
+        kn[j] = mine ? s_new[0][col] : u32x4{0u, 0u, 0u, 0u};
+        vn[j] = mine ? s_new[1][col] : u32x4{0u, 0u, 0u, 0u};
+      }
+      consume(kn, vn, ctx - 1, ctx);
     }
   }
 

@@ -249,7 +249,8 @@ pa_status_t decode_impl(void *out, const void *q, const void *key_cache, const v
                         int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                         float k_scale, float v_scale, int32_t partition_size, void *workspace,
                         size_t workspace_bytes, pa_dtype_t q_dt, pa_dtype_t kv_dt,
-                        hipStream_t stream) {
+                        hipStream_t stream, const void *new_k = nullptr,
+                        const void *new_v = nullptr) {
   Sizes z;
   pa_status_t st = plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                         max_context_len, partition_size, kv_dt, &z);
@@ -267,6 +268,10 @@ pa_status_t decode_impl(void *out, const void *q, const void *key_cache, const v
     return fail(PA_ERR_INVALID_ARGUMENT, "pointer arguments must not be NULL");
   if (!aligned16(out) || !aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache))
     return fail(PA_ERR_INVALID_ARGUMENT, "out, q and the pools must be 16-byte aligned");
+  if ((new_k == nullptr) != (new_v == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "key and value must both be given");
+  if (new_k && (!aligned16(new_k) || !aligned16(new_v)))
+    return fail(PA_ERR_INVALID_ARGUMENT, "key and value must be 16-byte aligned");
   if (z.ws_bytes > 0) {
     if (!workspace || workspace_bytes < z.ws_bytes)
       return fail(PA_ERR_WORKSPACE_TOO_SMALL,
@@ -299,6 +304,10 @@ pa_status_t decode_impl(void *out, const void *q, const void *key_cache, const v
   a.v_scale = v_scale;
   a.partition_size = z.partition;
   a.num_partitions = z.num_partitions;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.k_store = const_cast<void *>(key_cache);
+  a.v_store = const_cast<void *>(value_cache);
 
   hipError_t e = kv_dt == q_dt && pa::gqa_supported(q_dt, head_dim, num_heads, num_kv_heads)
                      ? pa::launch_decode_gqa(a, q_dt, stream)
@@ -325,6 +334,25 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
                      num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, 1.f, 1.f, partition_size,
                      workspace, workspace_bytes, dtype, dtype, stream);
+}
+
+pa_status_t pa_append_decode(void *out, const void *q, const void *key, const void *value,
+                             void *key_cache, void *value_cache, const int32_t *block_tables,
+                             const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t max_context_len, float scale, int32_t partition_size,
+                             void *workspace, size_t workspace_bytes, pa_dtype_t dtype,
+                             hipStream_t stream) {
+  if (dtype == PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED,
+                "E4M3 pools: write with pa_cache_write_fp8, then decode with pa_decode_fp8");
+  if (num_seqs > 0 && (!key || !value))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pointer arguments must not be NULL");
+  return decode_impl(out, q, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, 1.f, 1.f, partition_size,
+                     workspace, workspace_bytes, dtype, dtype, stream, key, value);
 }
 
 pa_status_t pa_decode_fp8(void *out, const void *q, const void *key_cache,

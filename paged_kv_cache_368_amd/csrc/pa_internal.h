@@ -60,6 +60,13 @@ struct DecodeArgs {
   float v_scale;             // the V pool scale for fp8 pools (1 otherwise)
   int partition_size;        // P
   int num_partitions;        // NP = ceil(max_context_len / P), >= 1
+  // Appending decode (null otherwise): token context_lens[s] - 1 of every
+  // sequence is new; its K/V rows [S][Hkv][D] are attended from here and
+  // written to the token's slot in the pools (k_store/v_store: the pools).
+  const void *new_k;
+  const void *new_v;
+  void *k_store;
+  void *v_store;
 };
 
 // kv_dt: the pools' storage type, equal to dt or kFP8 (dt fp16/bf16 only).

@@ -176,3 +176,24 @@ def test_copy_blocks_rejects(lib):
     assert cb(None, None, _p(), None, _p(), 2, 4096, 8, 8, None) == _capi.PA_ERR_INVALID_ARGUMENT
     assert cb(_p(8), None, _p(), None, _p(), 2, 4096, 8, 8, None) == _capi.PA_ERR_INVALID_ARGUMENT
     assert cb(None, None, None, None, None, 0, 4096, 8, 8, None) == _capi.PA_OK
+
+
+def test_append_decode_rejects(lib):
+    def call(**kw):
+        a = dict(out=_p(), q=_p(), key=_p(), value=_p(), k=_p(), v=_p(), bt=_p(), cl=_p(), S=2,
+                 H=8, Hkv=8, D=128, B=16, NB=64, MB=8, maxctx=128, scale=0.1, P=0, ws=None,
+                 wsb=0, dt=F16)
+        a.update(kw)
+        return lib.pa_append_decode(a["out"], a["q"], a["key"], a["value"], a["k"], a["v"],
+                                    a["bt"], a["cl"], a["S"], a["H"], a["Hkv"], a["D"], a["B"],
+                                    a["NB"], a["MB"], a["maxctx"], a["scale"], a["P"], a["ws"],
+                                    a["wsb"], a["dt"], None)
+    assert call(dt=FP8) == _capi.PA_ERR_UNSUPPORTED       # E4M3 pools take the two-call path
+    assert call(key=None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(value=None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(key=_p(264)) == _capi.PA_ERR_INVALID_ARGUMENT                # misaligned
+    assert call(H=6, Hkv=4) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(D=96) == _capi.PA_ERR_UNSUPPORTED
+    assert call(maxctx=200) == _capi.PA_ERR_INVALID_ARGUMENT             # > MB * B
+    assert call(P=16, maxctx=128) == _capi.PA_ERR_WORKSPACE_TOO_SMALL    # split needs workspace
+    assert call(S=0, out=None, q=None, key=None, value=None) == _capi.PA_OK
