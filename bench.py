@@ -50,10 +50,10 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # sources it was taken on (``sources`` = kernel_source_digest()); any change
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
-    "llama7b_f16/B16/P4096": {
-        "sources": "60c29e66d70908a136a353fa959470cc0a87d3f8a32c0a5cfa802a5299fdc1e0",
-        "fetch_kib": 328441.922, "fetch_scale": 1048576 / 524311.125,
-        "write_kib": 256.0, "write_scale": 1.0,
+    "llama7b_f16/B16/P4096/append": {
+        "sources": "2ead327b6d9de2222cd2b8f4bf52ea78ef7c56737b92ecf8981467fd3c82134e",
+        "fetch_kib": 328580.984, "fetch_scale": 1048576 / 524315.750,
+        "write_kib": 768.0, "write_scale": 1.0,
         "profile": "profiles/decode_mha_llama7b_f16.md"},
 }
 
