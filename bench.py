@@ -51,8 +51,8 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
     "llama7b_f16/B16/P4096/append": {
-        "sources": "2ead327b6d9de2222cd2b8f4bf52ea78ef7c56737b92ecf8981467fd3c82134e",
-        "fetch_kib": 328580.984, "fetch_scale": 1048576 / 524315.750,
+        "sources": "47b3af23d15960d97048128850f2a801294b93905d2dd2401a876cecb32ed2d2",
+        "fetch_kib": 328580.828, "fetch_scale": 1048576 / 524310.250,
         "write_kib": 768.0, "write_scale": 1.0,
         "profile": "profiles/decode_mha_llama7b_f16.md"},
 }

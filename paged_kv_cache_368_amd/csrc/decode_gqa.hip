@@ -36,10 +36,10 @@
 // from fp32 or bf16 limits, and the final o/l is independent of the
 // reference chosen.
 //
-// Appending decode: as on the vector kernel, the newest token's K/V rows come
-// from the input (the pool is streamed only up to the token before it, and
-// the new row is taken as one extra masked chunk after the loop) and the
-// work-group of the partition holding it stores them into its slot.
+// Appending decode: the newest token's K/V rows come from the input (staged in
+// LDS by the prologue and written over the pool's row in the chunk's LDS
+// tiles, so whatever the slot held before never counts), and the work-group
+// of the partition holding the token stores them into its slot.
 #include "pa_mfma.h"
 
 namespace pa {
@@ -169,17 +169,15 @@ void decode_gqa_kernel(DecodeArgs a) {
     return;
   }
 
-  // Tokens read from the pool: [t0, tp); the newest token, when appending,
-  // comes from LDS instead.
-  const bool holds_new = append && ctx > t0 && ctx <= t1;        // uniform
-  const int tp = holds_new ? ctx - 1 : t1;
-  const int nch = (tp - t0 + kChunk - 1) / kChunk;
+  const int nch = (t1 - t0 + kChunk - 1) / kChunk;
   const int nch_w = nch > wave ? (nch - wave + NW - 1) / NW : 0;
   int my_ids = 0;
   if (lane < nch_w) my_ids = s_tbl[((wave + NW * lane) * kChunk) >> a.log2_block];
 
-  const char *kbase = reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E;
-  const char *vbase = reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E;
+  const char *kbase =
+      scalar_ptr(reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E);
+  const char *vbase =
+      scalar_ptr(reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E);
   const int v_off = v_row * ROW + 16 * v_col;
   constexpr int kChunkBytes = kChunk * ROW;
 
@@ -224,12 +222,18 @@ void decode_gqa_kernel(DecodeArgs a) {
   // One 16-token chunk starting at token tc; rows at or past tend are masked.
   auto consume = [&](const u32x4 *kb, const u32x4 *vb, int tc, int tend) {
     const bool tail = tc + kChunk > tend;                // wave-uniform
+    // Appending: this chunk holds the newest token (wave-uniform); lanes
+    // 0..LPT-1 write its row over the pool's in the tiles.
+    const bool inject = append && tc < ctx && ctx <= tc + kChunk;
+    const int rn = ctx - 1 - tc;
     // K: through this wave's LDS tile into the A layout (lane l: token l%16,
     // bytes 64i + 16*(l/16) of its row).  Rows past the context are left as
     // they are: their scores are replaced by -inf below, by select.
 #pragma unroll
     for (int j = 0; j < VL; ++j)
       *reinterpret_cast<u32x4 *>(ktile + (v_row + j * TPL) * PITCH + 16 * v_col) = kb[j];
+    if (inject && lane < LPT)
+      *reinterpret_cast<u32x4 *>(ktile + rn * PITCH + 16 * lane) = s_new[0][lane];
     u32x4 ka[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i)
@@ -258,6 +262,8 @@ void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < VL; ++j)
       *reinterpret_cast<u32x4 *>(tile + (v_row + j * TPL) * PITCH + 16 * v_col) = vr[j];
+    if (inject && lane < LPT)
+      *reinterpret_cast<u32x4 *>(tile + rn * PITCH + 16 * lane) = s_new[1][lane];
 
     // Raise the reference only when some score exceeds it by kLazyMax: every
     // lane of a query column holds the column's m, so the test needs no
@@ -310,20 +316,9 @@ void decode_gqa_kernel(DecodeArgs a) {
         const int k = k0 + i;
         if (k >= nch_w) break;
         load(kb[(i + 1) % NBUF], vb[(i + 1) % NBUF], k + 1, last);
-        consume(kb[i], vb[i], t0 + (wave + NW * k) * kChunk, tp);
+        consume(kb[i], vb[i], t0 + (wave + NW * k) * kChunk, t1);
       }
     }
-  }
-  // The newest token as a chunk of one valid row (row 0, on wave 0).
-  if (holds_new && wave == 0) {
-    u32x4 kn[VL], vn[VL];
-#pragma unroll
-    for (int j = 0; j < VL; ++j) {
-      const bool mine = j == 0 && v_row == 0;
-      kn[j] = mine ? s_new[0][v_col] : u32x4{0u, 0u, 0u, 0u};
-      vn[j] = mine ? s_new[1][v_col] : u32x4{0u, 0u, 0u, 0u};
-    }
-    consume(kn, vn, ctx - 1, ctx);
   }
 
   // Column sums over the four lane groups.

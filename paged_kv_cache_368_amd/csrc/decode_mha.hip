@@ -247,8 +247,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   int my_ids = 0;
   if (lane < nch_w) my_ids = s_tbl[((wave + NW * lane) * kChunk) >> a.log2_block];
 
-  const char *kbase = reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E;
-  const char *vbase = reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E;
+  const char *kbase =
+      scalar_ptr(reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E);
+  const char *vbase =
+      scalar_ptr(reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E);
   const int lane_off = (row * D + col * EPL) * E;
 
   // Byte offset (from the kv head's first tile) of this wave's chunk k.

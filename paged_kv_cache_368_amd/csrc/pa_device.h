@@ -81,6 +81,18 @@ __device__ __forceinline__ void store_out(void *base, size_t elem, const float *
   }
 }
 
+// A pointer the caller knows to be the same in every lane, pinned to scalar
+// registers.  Buffer descriptors built from a base the compiler has placed in
+// VGPRs are wrapped in a per-load "waterfall" loop (readfirstlane, compare,
+// exec mask) around every buffer load; this keeps the base scalar.
+template <typename T>
+__device__ __forceinline__ T *scalar_ptr(T *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
 // Split-context partial states of the vector kernel (read once, by the merge
 // launch that follows): written through to memory with agent-scope stores
 // rather than left dirty in the XCD's L2.  Measured on a 32k-token, 64-way
