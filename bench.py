@@ -3,10 +3,10 @@
 One step = the whole decode hot path for one batch: the slot of each
 sequence's newest token, the write of its K/V into the pool, and paged
 attention over every context token.  By default the step is one call of
-pa_append_decode, which does all three in one launch (plus the log-sum-exp
-merge launch when partitions split a context); ``--step three`` times the
-same step as pa_compute_slots + pa_cache_write + pa_decode (always so for
-fp8 pools).
+pa_append_decode (pa_append_decode_fp8 for E4M3 pools), which does all three
+in one launch (plus the log-sum-exp merge launch when partitions split a
+context); ``--step three`` times the same step as pa_compute_slots +
+pa_cache_write(_fp8) + pa_decode(_fp8).
 
 Prints ONE JSON line.  ``value`` is context tokens per second (sum of
 context_lens over a step / step time) with every input already in HBM.
@@ -419,7 +419,7 @@ def main(argv=None) -> int:
     lib = pa.load_library()
     P_used = lib.pa_decode_partition_size(S, H, Hkv, D, B, maxctx, wl.partition_size, size_dt)
     ws_bytes = lib.pa_decode_workspace_size(S, H, Hkv, D, B, maxctx, wl.partition_size, size_dt)
-    fused = args.step == "fused" and not fp8
+    fused = args.step == "fused"
     nbytes = algorithmic_bytes(wl.context_lens, H, Hkv, D, B, dt, wl.pool_dtype,
                                new_row_write=fused)
     sum_ctx = int(wl.context_lens.sum())
@@ -443,9 +443,15 @@ def main(argv=None) -> int:
         if fused:
             if ev is not None:
                 ev[0].record(stream)
-            pa.pa_append_decode(base.out, base.q, base.new_key, base.new_value, kc, vc,
-                                base.block_tables, base.context_lens, maxctx, wl.scale,
-                                wl.partition_size, workspace)
+            if fp8:
+                pa.pa_append_decode_fp8(base.out, base.q, base.new_key, base.new_value, kc, vc,
+                                        base.block_tables, base.context_lens, maxctx,
+                                        wl.k_scale, wl.v_scale, wl.scale, wl.partition_size,
+                                        workspace)
+            else:
+                pa.pa_append_decode(base.out, base.q, base.new_key, base.new_value, kc, vc,
+                                    base.block_tables, base.context_lens, maxctx, wl.scale,
+                                    wl.partition_size, workspace)
             if ev is not None:
                 ev[1].record(stream)
             return
@@ -513,13 +519,14 @@ def main(argv=None) -> int:
                    "head_dim": D, "block_size": B, "sum_context_tokens": sum_ctx,
                    "max_context_len": maxctx, "partition_size": P_used, "seed": wl.seed,
                    "pool_copies_rotated": copies,
-                   "step": ("pa_append_decode: slot, K/V write and attention in one launch"
-                            if fused else "pa_compute_slots + pa_cache_write(_fp8) + "
+                   "step": ("pa_append_decode(_fp8): slot, K/V write and attention in one "
+                            "launch" if fused else "pa_compute_slots + pa_cache_write(_fp8) + "
                             "pa_decode(_fp8)")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(wl.name, B, P_used, fused),
                      "kernel": ("pa_append_decode" if fused else "pa_decode") +
+                               ("_fp8" if fp8 else "") +
                                " (decode kernel + merge pass when split)",
                      "bytes_per_launch": nbytes["total"], "mean_launch_us": dec_mean_s * 1e6,
                      "median_launch_us": dec_med_s * 1e6},

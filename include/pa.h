@@ -201,7 +201,7 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
  * output but does not stop the write, as with pa_cache_write).  The slot of the
  * newest token must not be shared with another sequence's context (copy a
  * shared last block first, pa_copy_blocks).  dtype PA_F32, PA_F16 or PA_BF16
- * (E4M3 pools: pa_cache_write_fp8, then pa_decode_fp8).
+ * (E4M3 pools: pa_append_decode_fp8).
  */
 pa_status_t pa_append_decode(void *out, const void *q, const void *key, const void *value,
                              void *key_cache, void *value_cache, const int32_t *block_tables,
@@ -211,6 +211,27 @@ pa_status_t pa_append_decode(void *out, const void *q, const void *key, const vo
                              int32_t max_context_len, float scale, int32_t partition_size,
                              void *workspace, size_t workspace_bytes, pa_dtype_t dtype,
                              hipStream_t stream);
+
+/*
+ * pa_append_decode_fp8 -- pa_append_decode over E4M3 pools: the newest
+ * token's rows (key/value, [num_seqs][num_kv_heads][head_dim] in q_dtype,
+ * PA_F16 or PA_BF16) are quantised with the pool scales exactly as
+ * pa_cache_write_fp8 does and stored in their slot, and out[s] is
+ * pa_decode_fp8's result over tokens 0..t with the newest token's stored
+ * codes.  Pools afterwards are bit-identical to pa_compute_slots +
+ * pa_cache_write_fp8 on the same inputs; other rules as pa_append_decode and
+ * pa_decode_fp8.
+ */
+pa_status_t pa_append_decode_fp8(void *out, const void *q, const void *key,
+                                 const void *value, void *key_cache, void *value_cache,
+                                 const int32_t *block_tables, const int32_t *context_lens,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 float scale, float k_scale, float v_scale,
+                                 int32_t partition_size, void *workspace,
+                                 size_t workspace_bytes, pa_dtype_t q_dtype,
+                                 hipStream_t stream);
 
 /*
  * pa_prefill -- paged attention for many query tokens per sequence (a prompt,

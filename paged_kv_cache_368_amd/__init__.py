@@ -16,6 +16,7 @@ from ._capi import (  # noqa: F401
     pa_copy_blocks,
     pa_compute_slots,
     pa_append_decode,
+    pa_append_decode_fp8,
     pa_decode,
     pa_decode_fp8,
     pa_decode_partition_size,

@@ -58,6 +58,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_append_decode.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32,
                                      i32, i32, i32, i32, c.c_float, i32, ptr, sz, c.c_int, ptr]
     lib.pa_append_decode.restype = st
+    lib.pa_append_decode_fp8.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32,
+                                         i32, i32, i32, i32, i32, c.c_float, c.c_float,
+                                         c.c_float, i32, ptr, sz, c.c_int, ptr]
+    lib.pa_append_decode_fp8.restype = st
     f32 = c.c_float
     lib.pa_cache_write_fp8.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, c.c_int,
                                        f32, f32, ptr]
@@ -377,6 +381,55 @@ def pa_append_decode(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor, valu
         ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(context_lens.data_ptr()),
         S, H, Hkv, D, B, NB, block_tables.shape[1], max_context_len, float(scale),
         partition_size, ws_ptr, ws_bytes, DTYPE_CODES[q.dtype], _stream(q)))
+    return out
+
+
+def pa_append_decode_fp8(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor,
+                         value: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor,
+                         max_context_len: int, k_scale: float, v_scale: float,
+                         scale: float | None = None, partition_size: int = 0,
+                         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """pa_append_decode over E4M3 pools (uint8 codes, value = code * scale):
+    the newest token's rows (``key``/``value`` [S][Hkv][D], q's type) are
+    quantised into their slot and attended; see include/pa.h."""
+    lib = load_library()
+    for n, t in (("out", out), ("q", q), ("key", key), ("value", value),
+                 ("key_cache", key_cache), ("value_cache", value_cache),
+                 ("block_tables", block_tables), ("context_lens", context_lens)):
+        _dev(t, n)
+    if q.dtype not in (torch.float16, torch.bfloat16) or any(
+            t.dtype != q.dtype for t in (out, key, value)):
+        raise ValueError("q, out, key and value must share float16 or bfloat16")
+    if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8:
+        raise ValueError("E4M3 pools are uint8 tensors of codes")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    S, H, D = q.shape
+    NB, Hkv, B, D2 = key_cache.shape
+    if D2 != D or tuple(value_cache.shape) != (NB, Hkv, B, D) or tuple(out.shape) != (S, H, D):
+        raise ValueError("shape mismatch between q, out and the pools")
+    if tuple(key.shape) != (S, Hkv, D) or tuple(value.shape) != (S, Hkv, D):
+        raise ValueError("key and value must be [num_seqs][num_kv_heads][head_dim]")
+    if block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables and context_lens must have one row per sequence")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    n = lib.pa_decode_workspace_size(S, H, Hkv, D, B, max_context_len, partition_size, PA_FP8_E4M3)
+    if n == ctypes.c_size_t(-1).value:
+        raise PaError(PA_ERR_INVALID_ARGUMENT, pa_last_error())
+    if n and workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_append_decode_fp8(
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(key.data_ptr()), ctypes.c_void_p(value.data_ptr()),
+        ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(context_lens.data_ptr()),
+        S, H, Hkv, D, B, NB, block_tables.shape[1], max_context_len, float(scale),
+        float(k_scale), float(v_scale), partition_size, ws_ptr, ws_bytes,
+        DTYPE_CODES[q.dtype], _stream(q)))
     return out
 
 

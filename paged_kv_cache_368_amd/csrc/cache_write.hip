@@ -58,29 +58,6 @@ __global__ __launch_bounds__(256) void compute_slots_kernel(
   slot_mapping[i] = slot;
 }
 
-// E4M3 code of a float32 value (the value already divided by the pool's
-// scale): nearest code with ties to the even code, magnitudes above 448
-// saturated to 448, NaN to 0x7F.  Done by exact power-of-two scaling and
-// rintf (round to nearest even on the integer grid of the target format), so
-// no hardware conversion mode is involved.
-__device__ __forceinline__ uint32_t e4m3_code(float x) {
-  const uint32_t bits = __builtin_bit_cast(uint32_t, x);
-  if ((bits & 0x7fffffffu) > 0x7f800000u) return 0x7fu;
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = fminf(__builtin_fabsf(x), 448.f);
-  uint32_t code;
-  if (a < 0x1p-6f) {
-    code = (uint32_t)__builtin_rintf(a * 512.f);             // subnormal grid, step 2^-9
-  } else {
-    const uint32_t ab = __builtin_bit_cast(uint32_t, a);
-    const int e = (int)(ab >> 23) - 127;                      // 2^e <= a < 2^(e+1), e in [-6, 8]
-    const float m = __builtin_bit_cast(float, (ab & 0x007fffffu) | 0x3f800000u);   // a / 2^e
-    const uint32_t mq = (uint32_t)__builtin_rintf((m - 1.f) * 8.f);   // 0..8; 8 carries
-    code = ((uint32_t)(e + 7) << 3) + mq;
-  }
-  return code | sign;
-}
-
 // Cache write into E4M3 pools: one thread converts 16 elements of a K row
 // (and of the matching V row) and stores their 16 codes with one 16-byte
 // store.  ST: the source rows' storage type.
@@ -113,30 +90,8 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(
     u32x4 w[SW];
 #pragma unroll
     for (int j = 0; j < SW; ++j) w[j] = reinterpret_cast<const u32x4 *>(in)[j];
-    float x[16];
-#pragma unroll
-    for (int j = 0; j < SW; ++j) {
-      const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (ST == kF32) {
-          x[4 * j + k] = as_f32(ww[k]);
-        } else {
-          x[8 * j + 2 * k] = lo_f32<ST>(ww[k]);
-          x[8 * j + 2 * k + 1] = hi_f32<ST>(ww[k]);
-        }
-      }
-    }
-    uint32_t out[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) word |= e4m3_code(x[4 * k + b] / scale) << (8 * b);
-      out[k] = word;
-    }
     *reinterpret_cast<u32x4 *>((which == 0 ? key_cache : value_cache) + dst) =
-        u32x4{out[0], out[1], out[2], out[3]};
+        e4m3_codes16<ST>(w, scale);
   }
 }
 

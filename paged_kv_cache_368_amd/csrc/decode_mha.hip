@@ -177,17 +177,35 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   for (int i = 0; i < QW; ++i)
     qv[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.q) +
                                              (row_out + col * EPL) * EQ + 16 * i);
-  constexpr bool kCanAppend = KT != kFP8;
-  const bool append = kCanAppend && a.new_k != nullptr;        // uniform (kernel argument)
-  // Lanes 0..LPT-1 (wave 0, row 0) hold the newest token's rows.
-  const bool new_lane = append && tid < LPT;
-  u32x4 nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
-  if (new_lane) {
-    const size_t new_off = (((size_t)s * a.num_kv_heads + kvh) * D + col * EPL) * E;
-    nk = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.new_k) + new_off);
-    nv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.new_v) + new_off);
-    s_new[0][col] = nk;
-    s_new[1][col] = nv;
+  const bool append = a.new_k != nullptr;                      // uniform (kernel argument)
+  // The newest token's K and V rows go to LDS (s_new) for the extra chunk and
+  // the slot write.  Pools of the query's type: lanes 0..LPT-1 of wave 0 copy
+  // their 16-byte slices.  E4M3 pools: the rows arrive in the query's type
+  // and are quantised here exactly as the separate cache write does, four
+  // elements per lane over the whole of wave 0 (K on lanes 0..D/4-1, V on the
+  // next D/4), so the conversion stays short next to the prologue's loads.
+  if (append && wave == 0) {
+    const size_t row_in = ((size_t)s * a.num_kv_heads + kvh) * D * EQ;
+    if constexpr (KT == kFP8) {
+      constexpr int NE = D / 4;
+      if (lane < 2 * NE) {
+        const bool isv = lane >= NE;
+        const int w = isv ? lane - NE : lane;
+        const u32x2 raw = *reinterpret_cast<const u32x2 *>(
+            static_cast<const char *>(isv ? a.new_v : a.new_k) + row_in + 4 * w * EQ);
+        const float sc = isv ? a.v_scale : a.k_scale;
+        const uint32_t word = e4m3_code(lo_f32<DT>(raw.x) / sc) |
+                              (e4m3_code(hi_f32<DT>(raw.x) / sc) << 8) |
+                              (e4m3_code(lo_f32<DT>(raw.y) / sc) << 16) |
+                              (e4m3_code(hi_f32<DT>(raw.y) / sc) << 24);
+        reinterpret_cast<uint32_t *>(&s_new[isv ? 1 : 0][0])[w] = word;
+      }
+    } else if (lane < LPT) {
+      s_new[0][col] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.new_k) +
+                                                       row_in + 16 * col);
+      s_new[1][col] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.new_v) +
+                                                       row_in + 16 * col);
+    }
   }
 
   const bool bad_ctx = ctx < 0 || ctx > a.max_context_len ||
@@ -210,14 +228,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   const size_t block_stride = head_stride * a.num_kv_heads;
   // Like the separate cache write, it needs only the token's own slot to be
   // valid (a bad id elsewhere in the table poisons the output, not the write).
-  if (new_lane && !bad_ctx && ctx > t0 && ctx <= t1 && h % G == 0) {
+  if (append && tid < LPT && !bad_ctx && ctx > t0 && ctx <= t1 && h % G == 0) {
     const int tn = ctx - 1;
     const int phys = s_tbl[(tn - t0) >> a.log2_block];
     if (phys >= 0 && phys < a.num_blocks) {
       const size_t dst = ((size_t)phys * block_stride + kvh * head_stride +
                           (size_t)(tn & (a.block_size - 1)) * D + col * EPL) * E;
-      *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_store) + dst) = nk;
-      *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_store) + dst) = nv;
+      *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_store) + dst) = s_new[0][col];
+      *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_store) + dst) = s_new[1][col];
     }
   }
   if (poison) {
@@ -343,18 +361,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
       }
     }
   }
-  if constexpr (kCanAppend) {
-    // The newest token as a chunk of one valid row (row 0 of wave 0).
-    if (holds_new && wave == 0) {
-      u32x4 kn[NL], vn[NL];
+  // The newest token as a chunk of one valid row (row 0 of wave 0).
+  if (holds_new && wave == 0) {
+    u32x4 kn[NL], vn[NL];
 #pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const bool mine = j == 0 && row == 0;
-        kn[j] = mine ? s_new[0][col] : u32x4{0u, 0u, 0u, 0u};
-        vn[j] = mine ? s_new[1][col] : u32x4{0u, 0u, 0u, 0u};
-      }
-      consume(kn, vn, ctx - 1, ctx);
+    for (int j = 0; j < NL; ++j) {
+      const bool mine = j == 0 && row == 0;
+      kn[j] = mine ? s_new[0][col] : u32x4{0u, 0u, 0u, 0u};
+      vn[j] = mine ? s_new[1][col] : u32x4{0u, 0u, 0u, 0u};
     }
+    consume(kn, vn, ctx - 1, ctx);
   }
 
   // Merge the rows of this wave (lanes with equal col, different row).

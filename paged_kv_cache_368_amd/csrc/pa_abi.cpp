@@ -301,6 +301,7 @@ pa_status_t decode_impl(void *out, const void *q, const void *key_cache, const v
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
   a.scale_log2 = scale * 1.4426950408889634f * k_scale;
+  a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.partition_size = z.partition;
   a.num_partitions = z.num_partitions;
@@ -345,14 +346,34 @@ pa_status_t pa_append_decode(void *out, const void *q, const void *key, const vo
                              void *workspace, size_t workspace_bytes, pa_dtype_t dtype,
                              hipStream_t stream) {
   if (dtype == PA_FP8_E4M3)
-    return fail(PA_ERR_UNSUPPORTED,
-                "E4M3 pools: write with pa_cache_write_fp8, then decode with pa_decode_fp8");
+    return fail(PA_ERR_UNSUPPORTED, "E4M3 pools are appended by pa_append_decode_fp8");
   if (num_seqs > 0 && (!key || !value))
     return fail(PA_ERR_INVALID_ARGUMENT, "pointer arguments must not be NULL");
   return decode_impl(out, q, key_cache, value_cache, block_tables, context_lens, num_seqs,
                      num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, 1.f, 1.f, partition_size,
                      workspace, workspace_bytes, dtype, dtype, stream, key, value);
+}
+
+pa_status_t pa_append_decode_fp8(void *out, const void *q, const void *key,
+                                 const void *value, void *key_cache, void *value_cache,
+                                 const int32_t *block_tables, const int32_t *context_lens,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 float scale, float k_scale, float v_scale,
+                                 int32_t partition_size, void *workspace,
+                                 size_t workspace_bytes, pa_dtype_t q_dtype,
+                                 hipStream_t stream) {
+  if (q_dtype != PA_F16 && q_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_append_decode_fp8 takes fp16 or bf16 queries and rows");
+  if (num_seqs > 0 && (!key || !value))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pointer arguments must not be NULL");
+  return decode_impl(out, q, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, q_dtype, PA_FP8_E4M3, stream,
+                     key, value);
 }
 
 pa_status_t pa_decode_fp8(void *out, const void *q, const void *key_cache,

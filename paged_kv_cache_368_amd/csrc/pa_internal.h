@@ -57,6 +57,7 @@ struct DecodeArgs {
   int num_seqs, num_heads, num_kv_heads, head_dim;
   int block_size, log2_block, num_blocks, max_blocks_per_seq, max_context_len;
   float scale_log2;          // scale * log2(e) (* the K pool scale for fp8 pools): base-2 scores
+  float k_scale;             // the K pool scale for fp8 pools (1 otherwise)
   float v_scale;             // the V pool scale for fp8 pools (1 otherwise)
   int partition_size;        // P
   int num_partitions;        // NP = ceil(max_context_len / P), >= 1

@@ -11,7 +11,6 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma_k32(const u32x4 &a, const u32x4 &b, const f32x4 &c) {

@@ -197,3 +197,23 @@ def test_append_decode_rejects(lib):
     assert call(maxctx=200) == _capi.PA_ERR_INVALID_ARGUMENT             # > MB * B
     assert call(P=16, maxctx=128) == _capi.PA_ERR_WORKSPACE_TOO_SMALL    # split needs workspace
     assert call(S=0, out=None, q=None, key=None, value=None) == _capi.PA_OK
+
+
+def test_append_decode_fp8_rejects(lib):
+    def call(**kw):
+        a = dict(out=_p(), q=_p(), key=_p(), value=_p(), k=_p(), v=_p(), bt=_p(), cl=_p(), S=2,
+                 H=8, Hkv=8, D=128, B=16, NB=64, MB=8, maxctx=128, scale=0.1, ks=0.5, vs=0.5,
+                 P=0, ws=None, wsb=0, dt=F16)
+        a.update(kw)
+        return lib.pa_append_decode_fp8(a["out"], a["q"], a["key"], a["value"], a["k"], a["v"],
+                                        a["bt"], a["cl"], a["S"], a["H"], a["Hkv"], a["D"],
+                                        a["B"], a["NB"], a["MB"], a["maxctx"], a["scale"],
+                                        a["ks"], a["vs"], a["P"], a["ws"], a["wsb"], a["dt"],
+                                        None)
+    assert call(dt=F32) == _capi.PA_ERR_UNSUPPORTED
+    assert call(dt=FP8) == _capi.PA_ERR_UNSUPPORTED
+    assert call(key=None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(ks=-1.0) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(vs=float("inf")) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(value=_p(264)) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(S=0, out=None, q=None, key=None, value=None) == _capi.PA_OK

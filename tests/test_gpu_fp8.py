@@ -142,3 +142,35 @@ def test_decode_fp8_full_size_sampled():
     idx = tuple(np.array(pairs).T)
     BD.assert_close(got[idx], ref[idx], "f16", "llama7b fp8 sample")
     assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("qt", ["f16", "bf16"])
+@pytest.mark.parametrize("name,kw", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_append_decode_fp8_matches_oracle(name, kw, qt):
+    """One-launch step over E4M3 pools: the newest token's rows quantised
+    into their slot (bit-exact against the oracle's quantising cache write)
+    and attended with the stored codes; the slot holds NaN codes before."""
+    wl = build(f"fp8app_{name}", qt, kw["ctx"], kw["H"], kw["Hkv"], kw["D"], kw["B"], seed=18,
+               pool="choice", pool_factor=1.5, value_scale=0.5, kv_dtype="fp8", kv_scale=0.375)
+    slots = P.compute_slots(wl.block_tables, wl.block_size, wl.num_blocks,
+                            context_lens=wl.context_lens)
+    for sl in slots:
+        b, off = divmod(int(sl), wl.block_size)
+        wl.key_cache[b, :, off, :] = 0x7F
+        wl.value_cache[b, :, off, :] = 0xFF
+    kc, vc = wl.key_cache.copy(), wl.value_cache.copy()
+    P.cache_write_fp8(kc, vc, wl.new_key, wl.new_value, slots, wl.block_size, qt, wl.k_scale,
+                      wl.v_scale)
+    ref = P.paged_decode_fp8(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.block_size,
+                             wl.scale, qt, wl.k_scale, wl.v_scale, wl.num_kv_heads)
+    for ps in (0, 64):
+        _say(f"fp8 append {name} {qt} P={ps}")
+        dev = to_device(wl)
+        pa.pa_append_decode_fp8(dev.out, dev.q, dev.new_key, dev.new_value, dev.key_cache,
+                                dev.value_cache, dev.block_tables, dev.context_lens,
+                                wl.max_context_len, wl.k_scale, wl.v_scale, wl.scale, ps)
+        torch.cuda.synchronize()
+        got = P.to_f64(from_torch(dev.out, qt), qt)
+        BD.assert_close(got, ref, qt, f"{name} P={ps}")
+        assert np.array_equal(from_torch(dev.key_cache, "fp8"), kc), f"{name} P={ps}: K codes"
+        assert np.array_equal(from_torch(dev.value_cache, "fp8"), vc), f"{name} P={ps}: V codes"
