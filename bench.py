@@ -51,8 +51,8 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
     "llama7b_f16/B16/P4096/append": {
-        "sources": "47b3af23d15960d97048128850f2a801294b93905d2dd2401a876cecb32ed2d2",
-        "fetch_kib": 328580.828, "fetch_scale": 1048576 / 524310.250,
+        "sources": "9356cab4af49ef78305287985a6a67d13c82db7a74deac2e5b269ec169b44d1a",
+        "fetch_kib": 328580.797, "fetch_scale": 1048576 / 524315.312,
         "write_kib": 768.0, "write_scale": 1.0,
         "profile": "profiles/decode_mha_llama7b_f16.md"},
 }
