@@ -383,6 +383,8 @@ def main(argv=None) -> int:
     ap.add_argument("--step", choices=["fused", "three"], default="fused",
                     help="decode step as one pa_append_decode call (default) or as "
                          "pa_compute_slots + pa_cache_write + pa_decode")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the STREAM-like read ceiling measured after the timed steps")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     args = ap.parse_args(argv)
@@ -492,6 +494,25 @@ def main(argv=None) -> int:
           f"median {dec_med_s * 1e6:.1f} us p10 {dec_ms[len(dec_ms) // 10] * 1e3:.1f} us "
           f"p90 {dec_ms[(9 * len(dec_ms)) // 10] * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    ceiling = None
+    if not args.no_ceiling:
+        # A STREAM-like read ceiling on the same box: torch's sum over 2 GiB of
+        # fp16 (contiguous reads, negligible writes), best of 10 passes.
+        big = torch.ones(1 << 30, dtype=torch.float16, device="cuda")
+        big.sum()
+        best = float("inf")
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            big.sum()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / 1e3)
+        ceiling = {"gbps": big.numel() * 2 / best / 1e9,
+                   "how": "torch.sum over 2 GiB of fp16 on the same stream, best of 10"}
+        del big
+        torch.cuda.synchronize()
+
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -529,7 +550,10 @@ def main(argv=None) -> int:
                                ("_fp8" if fp8 else "") +
                                " (decode kernel + merge pass when split)",
                      "bytes_per_launch": nbytes["total"], "mean_launch_us": dec_mean_s * 1e6,
-                     "median_launch_us": dec_med_s * 1e6},
+                     "median_launch_us": dec_med_s * 1e6,
+                     "p10_launch_us": dec_ms[len(dec_ms) // 10] * 1e3,
+                     "p90_launch_us": dec_ms[(9 * len(dec_ms)) // 10] * 1e3},
+        "read_ceiling": ceiling,
         "decode_context_tokens_per_s": sum_ctx / dec_mean_s,
         "device": dev_name,
     }

@@ -7,11 +7,13 @@
 // found through block_tables[s] (P3 §2-§3).  A prefix cached earlier (P3 §3,
 // shared prefixes save prefill work) is simply not among the queries.
 //
-// Work decomposition: one work-group of 4 waves per (sequence, 64-row query
-// tile, query head); wave w owns rows 16w .. 16w+15 of the tile, so each
-// wave holds the complete softmax state of its rows and no cross-wave merge
-// is needed.  The work-group walks the context in 32-token chunks that all
-// four waves share:
+// Work decomposition: one work-group of 4 waves per (sequence, 128-row query
+// tile, query head); wave w owns rows 32w .. 32w+31 of the tile as two
+// 16-row subtiles, so each wave holds the complete softmax state of its rows
+// and no cross-wave merge is needed.  Every K and V operand read from LDS
+// feeds both subtiles' products, which halves the LDS traffic per flop
+// against one subtile per wave.  The work-group walks the context in
+// 32-token chunks that all four waves share:
 //
 //   * K and V of a chunk go from HBM straight into LDS (buffer loads with
 //     the LDS bit: no registers), each wave moving a quarter of it, into one
@@ -40,7 +42,8 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyMax = 8.f;          // log2 units: weights stay <= 256
 constexpr int kPfWaves = 4;
-constexpr int kRows = 16 * kPfWaves;     // query rows per work-group
+constexpr int kSub = 2;                  // 16-row subtiles per wave
+constexpr int kRows = 16 * kSub * kPfWaves;   // query rows per work-group
 constexpr int kCh = 32;                  // tokens per chunk
 constexpr int kWindow = kMaxPartition;   // tokens whose block ids are staged at once
 // s_waitcnt immediate for vmcnt(0) (expcnt and lgkmcnt left at their
@@ -51,8 +54,10 @@ constexpr int kWaitVmcnt0 = 0x0f70;
 template <int DT>
 __device__ __forceinline__ uint32_t pack_p(float a, float b) {
   if constexpr (DT == kF16) {
-    const _Float16 x = (_Float16)a, y = (_Float16)b;                  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    // one v_cvt_pk_f16_f32, round to nearest even
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
   } else {
     return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a),
                                  0x07060302u);                         // truncated high halves
@@ -122,23 +127,30 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
   const int nrows = min(kRows, qlen - r0);
   const int pos0 = ctx - qlen + r0;          // position of the tile's first row
   const int t1 = pos0 + nrows;               // tokens the tile attends to
-  // This wave's rows: wr0 .. wr0 + wrows - 1 of the tile (wrows may be 0).
-  const int wr0 = 16 * wave;
-  const int wrows = max(0, min(16, nrows - wr0));
+  // This wave's rows: wr0 .. wr0 + wrows - 1 of the tile (wrows may be 0);
+  // subtile u holds rows wr0 + 16u .. + srows[u] - 1.
+  const int wr0 = 16 * kSub * wave;
+  const int wrows = max(0, min(16 * kSub, nrows - wr0));
   const int wpos0 = pos0 + wr0;              // position of the wave's first row
   const int wlast = pos0 + wr0 + max(wrows, 1) - 1;
-  const int cpos = pos0 + wr0 + min(c16, max(wrows, 1) - 1);   // causal limit of column c16
+  int srows[kSub], cpos[kSub];
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) {
+    srows[u] = max(0, min(16, nrows - wr0 - 16 * u));
+    cpos[u] = pos0 + wr0 + 16 * u + min(c16, max(srows[u], 1) - 1);   // causal limit of column c16
+  }
 
-  u32x4 qf[KI];
-  {
-    const bool live = c16 < wrows;
+  u32x4 qf[kSub][KI];
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) {
+    const bool live = c16 < srows[u];
     const char *qrow = reinterpret_cast<const char *>(a.q) +
-                       ((size_t)(q0 + r0 + wr0 + (live ? c16 : 0)) * H + h) * ROW;
+                       ((size_t)(q0 + r0 + wr0 + 16 * u + (live ? c16 : 0)) * H + h) * ROW;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
       if (live) v = *reinterpret_cast<const u32x4 *>(qrow + 64 * i + 16 * g4);
-      qf[i] = v;
+      qf[u][i] = v;
     }
   }
 
@@ -166,10 +178,21 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
     return row * ROW + (((lb >> 4) ^ (row % PIECES)) << 4) + (lb & 15);
   };
 
-  float m = kNegInf, l = 0.f;
-  f32x4 o[NT];
+  // Row sums of the weights come from the matrix cores too: P times a
+  // 32x16 matrix of ones puts row 4g4+r's sum in lsum[u][r] of every lane of
+  // group g4, the layout of the output tiles (and of the weights as they
+  // enter the products, so numerator and denominator use the same values).
+  constexpr uint32_t kOnes = DT == kF16 ? 0x3C003C00u : 0x3F803F80u;
+  const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
+  float m[kSub];
+  f32x4 o[kSub][NT], lsum[kSub];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < kSub; ++u) {
+    m[u] = kNegInf;
+    lsum[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[u][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   bool poison = false;
   for (int w0 = 0; w0 < t1; w0 += kWindow) {
@@ -223,58 +246,68 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
       const int tc = w0 + k * kCh;
       if (wrows == 0 || tc > wlast) return;      // uniform: the chunk is after this wave's rows
       const bool diag = tc + kCh - 1 > wpos0;
-      float sc[2][4];
+      float sc[kSub][2][4];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[kSub];
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
           const u32x4 ka = *reinterpret_cast<const u32x4 *>(sk + k_addr(tt, i));
-          acc = mfma_k32<DT>(ka, qf[i], acc);
+#pragma unroll
+          for (int u = 0; u < kSub; ++u) acc[u] = mfma_k32<DT>(ka, qf[u][i], acc[u]);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[tt][r] = acc[r] * a.scale_log2;
+        for (int u = 0; u < kSub; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[u][tt][r] = acc[u][r] * a.scale_log2;
       }
       if (diag) {
 #pragma unroll
+        for (int u = 0; u < kSub; ++u)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (tc + 16 * tt + 4 * g4 + r > cpos[u]) sc[u][tt][r] = kNegInf;
+      }
+      u32x4 pa_hi[kSub], pa_lo[kSub];
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        float mloc = sc[u][0][0];
+#pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (tc + 16 * tt + 4 * g4 + r > cpos) sc[tt][r] = kNegInf;
-      }
-      float mloc = sc[0][0];
+          for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[u][tt][r]);
+        if (__builtin_amdgcn_ballot_w64(mloc > m[u] + kLazyMax)) {
+          const float cm = max_xor32(max_xor16(mloc));
+          const float mnew = fmaxf(m[u], cm);
+          const float corr = mnew == kNegInf ? 1.f : exp2_fast(m[u] - mnew);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+          for (int r = 0; r < 4; ++r) {
+            const float cr = __shfl(corr, 4 * g4 + r);
+            lsum[u][r] *= cr;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[tt][r]);
-      if (__builtin_amdgcn_ballot_w64(mloc > m + kLazyMax)) {
-        const float cm = max_xor32(max_xor16(mloc));
-        const float mnew = fmaxf(m, cm);
-        const float corr = mnew == kNegInf ? 1.f : exp2_fast(m - mnew);
-        l *= corr;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float cr = __shfl(corr, 4 * g4 + r);
-#pragma unroll
-          for (int n = 0; n < NT; ++n) o[n][r] *= cr;
+            for (int n = 0; n < NT; ++n) o[u][n][r] *= cr;
+          }
+          m[u] = mnew;
         }
-        m = mnew;
+        const float msafe = m[u] == kNegInf ? 0.f : m[u];
+        float p[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[tt][r] = exp2_fast(sc[u][tt][r] - msafe);
+        pa_hi[u] = u32x4{pack_p<DT>(p[0][0], p[0][1]), pack_p<DT>(p[0][2], p[0][3]),
+                         pack_p<DT>(p[1][0], p[1][1]), pack_p<DT>(p[1][2], p[1][3])};
+        pa_lo[u] = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (DT == kBF16)
+          pa_lo[u] = u32x4{pack_lo_bf16(p[0][0], p[0][1]), pack_lo_bf16(p[0][2], p[0][3]),
+                           pack_lo_bf16(p[1][0], p[1][1]), pack_lo_bf16(p[1][2], p[1][3])};
+        lsum[u] = mfma_k32<DT>(pa_hi[u], ones, lsum[u]);
+        if constexpr (DT == kBF16) lsum[u] = mfma_k32<DT>(pa_lo[u], ones, lsum[u]);
       }
-      const float msafe = m == kNegInf ? 0.f : m;
-      float p[2][4];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[tt][r] = exp2_fast(sc[tt][r] - msafe);
-          l += p[tt][r];
-        }
-      const u32x4 pa_hi = {pack_p<DT>(p[0][0], p[0][1]), pack_p<DT>(p[0][2], p[0][3]),
-                           pack_p<DT>(p[1][0], p[1][1]), pack_p<DT>(p[1][2], p[1][3])};
-      u32x4 pa_lo = {0u, 0u, 0u, 0u};
-      if constexpr (DT == kBF16)
-        pa_lo = u32x4{pack_lo_bf16(p[0][0], p[0][1]), pack_lo_bf16(p[0][2], p[0][3]),
-                      pack_lo_bf16(p[1][0], p[1][1]), pack_lo_bf16(p[1][2], p[1][3])};
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -283,8 +316,11 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
             (__attribute__((address_space(3))) s16x4 *)(sv + v_addr(1, n)));
         const u32x2 w0v = __builtin_bit_cast(u32x2, v0), w1v = __builtin_bit_cast(u32x2, v1);
         const u32x4 vf = {w0v.x, w0v.y, w1v.x, w1v.y};
-        o[n] = mfma_k32<DT>(pa_hi, vf, o[n]);
-        if constexpr (DT == kBF16) o[n] = mfma_k32<DT>(pa_lo, vf, o[n]);
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {
+          o[u][n] = mfma_k32<DT>(pa_hi[u], vf, o[u][n]);
+          if constexpr (DT == kBF16) o[u][n] = mfma_k32<DT>(pa_lo[u], vf, o[u][n]);
+        }
       }
     };
 
@@ -311,19 +347,21 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
   }
   if (wrows == 0) return;
 
-  // Row sums over the four lane groups, then out = O / l for each row this
-  // lane holds (rows 4*g4 + r of the wave, dims 16n + c16).
-  l = sum_xor32(sum_xor16(l));
+  // out = O / l for each row this lane holds (rows 4*g4 + r of subtile u,
+  // dims 16n + c16).
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int q = 4 * g4 + r;
-    const float lr = __shfl(l, q);
-    if (q < wrows) {
-      const size_t rowbase = ((size_t)(q0 + r0 + wr0 + q) * H + h) * D;
+  for (int u = 0; u < kSub; ++u) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const float v = lr == 0.f ? 0.f : o[n][r] / lr;
-        store_out<DT>(a.out, rowbase + 16 * n + c16, &v, 1);
+    for (int r = 0; r < 4; ++r) {
+      const int q = 4 * g4 + r;
+      const float lr = lsum[u][r];
+      if (q < srows[u]) {
+        const size_t rowbase = ((size_t)(q0 + r0 + wr0 + 16 * u + q) * H + h) * D;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const float v = lr == 0.f ? 0.f : o[u][n][r] / lr;
+          store_out<DT>(a.out, rowbase + 16 * n + c16, &v, 1);
+        }
       }
     }
   }
