@@ -502,21 +502,27 @@ def main(argv=None) -> int:
 
     ceiling = None
     if not args.no_ceiling:
-        # A STREAM-like read ceiling on the same box: torch's sum over 2 GiB of
-        # fp16 (contiguous reads, negligible writes), best of 10 passes.
-        big = torch.ones(1 << 30, dtype=torch.float16, device="cuda")
-        big.sum()
-        best = float("inf")
-        for _ in range(10):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            big.sum()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            best = min(best, e0.elapsed_time(e1) / 1e3)
-        ceiling = {"gbps": big.numel() * 2 / best / 1e9,
-                   "how": "torch.sum over 2 GiB of fp16 on the same stream, best of 10"}
-        del big
+        # The achievable read rate on this machine (pa_read_probe over 2 GiB):
+        # in index order, and as 4 KB tiles in random order, the decode
+        # kernels' pattern (one (block, kv head) tile of K or V at a time).
+        big = torch.ones(1 << 29, dtype=torch.int32, device="cuda")
+        sink = torch.empty(pa.PA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+        perm = torch.randperm(big.numel() * 4 // 4096, device="cuda",
+                              generator=torch.Generator(device="cuda").manual_seed(0)).int()
+        ceiling = {"how": "pa_read_probe over 2 GiB, best of 5 HIP-event-timed calls"}
+        for key, order in (("contiguous_gbps", None), ("random_4k_tiles_gbps", perm)):
+            pa.pa_read_probe(big, 4096, order, sink)
+            best = float("inf")
+            for _ in range(5):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                pa.pa_read_probe(big, 4096, order, sink)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                best = min(best, e0.elapsed_time(e1) / 1e3)
+            ceiling[key] = big.numel() * 4 / best / 1e9
+        del big, perm, sink
         torch.cuda.synchronize()
 
     if args.copy_calibration_mib:
@@ -560,6 +566,7 @@ def main(argv=None) -> int:
                      "p10_launch_us": dec_ms[len(dec_ms) // 10] * 1e3,
                      "p90_launch_us": dec_ms[(9 * len(dec_ms)) // 10] * 1e3},
         "read_ceiling": ceiling,
+        "frac_of_tile_ceiling": (achieved / ceiling["random_4k_tiles_gbps"]) if ceiling else None,
         "decode_context_tokens_per_s": sum_ctx / dec_mean_s,
         "device": dev_name,
     }

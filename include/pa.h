@@ -345,6 +345,26 @@ pa_status_t pa_copy_blocks(void *dst_k, void *dst_v, const void *src_k, const vo
                            const int32_t *block_pairs, int32_t num_pairs, int64_t block_bytes,
                            int32_t dst_num_blocks, int32_t src_num_blocks, hipStream_t stream);
 
+/*
+ * pa_read_probe -- the achievable HBM read rate for a tiled pattern, to set
+ * beside the nominal peak (the decode kernels read 4 KB (block, kv head)
+ * tiles of K and V in table order, i.e. scattered).  Reads num_tiles tiles of
+ * tile_bytes from buf in the order given (order[i] = index of the i-th tile
+ * read; NULL reads them in index order; entries outside [0, num_tiles) are
+ * clamped), 16-byte non-temporal loads, 1 KB per wave load, and writes per
+ * work-group the XOR of every 32-bit word it read to sink (so the XOR of all
+ * sink words is the XOR of the buffer when order is a permutation).
+ *
+ *   buf       in   device, >= tile_bytes * num_tiles bytes, 16-byte aligned
+ *   order     in   device int32 [num_tiles] or NULL
+ *   sink      out  device, PA_READ_PROBE_SINK_WORDS uint32 words, overwritten
+ *
+ * tile_bytes must be a positive multiple of 1024.  The caller times the call.
+ */
+#define PA_READ_PROBE_SINK_WORDS 2048
+pa_status_t pa_read_probe(const void *buf, int64_t tile_bytes, int64_t num_tiles,
+                          const int32_t *order, uint32_t *sink, hipStream_t stream);
+
 /* Text of the last non-OK status returned on the calling thread. */
 const char *pa_last_error(void);
 

@@ -11,6 +11,7 @@ from ._capi import (  # noqa: F401
     declared_functions,
     load_library,
     PA_FP8_E4M3,
+    PA_READ_PROBE_SINK_WORDS,
     pa_cache_write,
     pa_cache_write_fp8,
     pa_copy_blocks,
@@ -23,5 +24,6 @@ from ._capi import (  # noqa: F401
     pa_decode_workspace_size,
     pa_last_error,
     pa_prefill,
+    pa_read_probe,
     pa_version,
 )

@@ -58,6 +58,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_append_decode.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32,
                                      i32, i32, i32, i32, c.c_float, i32, ptr, sz, c.c_int, ptr]
     lib.pa_append_decode.restype = st
+    lib.pa_read_probe.argtypes = [ptr, c.c_int64, c.c_int64, ptr, ptr, ptr]
+    lib.pa_read_probe.restype = st
     lib.pa_append_decode_fp8.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32,
                                          i32, i32, i32, i32, i32, c.c_float, c.c_float,
                                          c.c_float, i32, ptr, sz, c.c_int, ptr]
@@ -431,6 +433,32 @@ def pa_append_decode_fp8(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor,
         float(k_scale), float(v_scale), partition_size, ws_ptr, ws_bytes,
         DTYPE_CODES[q.dtype], _stream(q)))
     return out
+
+
+PA_READ_PROBE_SINK_WORDS = 2048
+
+
+def pa_read_probe(buf: torch.Tensor, tile_bytes: int, order: torch.Tensor | None = None,
+                  sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Read ``buf`` as tiles of ``tile_bytes`` in ``order`` (int32 tile
+    indices; None: index order) with the library's read probe; returns the
+    sink (one uint32 fold per work-group).  The caller times the call."""
+    lib = load_library()
+    _dev(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if tile_bytes <= 0 or tile_bytes % 1024:
+        raise ValueError("tile_bytes must be a positive multiple of 1024")
+    n = nbytes // tile_bytes
+    if order is not None:
+        _dev(order, "order")
+        if order.dtype != torch.int32 or order.numel() != n:
+            raise ValueError("order must be int32 with one entry per tile")
+    if sink is None:
+        sink = torch.empty(PA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    _check(lib.pa_read_probe(ctypes.c_void_p(buf.data_ptr()), tile_bytes, n,
+                             ctypes.c_void_p(order.data_ptr()) if order is not None else None,
+                             ctypes.c_void_p(sink.data_ptr()), _stream(buf)))
+    return sink
 
 
 def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["pa_abi.cpp", "block_manager.cpp", "decode_mha.hip", "decode_gqa.hip", "cache_write.hip", "block_copy.hip", "prefill.hip"]
+SOURCES = ["pa_abi.cpp", "block_manager.cpp", "decode_mha.hip", "decode_gqa.hip", "cache_write.hip", "block_copy.hip", "prefill.hip", "read_probe.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -474,4 +474,17 @@ pa_status_t pa_cache_write_fp8(const void *key, const void *value, void *key_cac
   return PA_OK;
 }
 
+pa_status_t pa_read_probe(const void *buf, int64_t tile_bytes, int64_t num_tiles,
+                          const int32_t *order, uint32_t *sink, hipStream_t stream) {
+  if (tile_bytes <= 0 || tile_bytes % 1024 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "tile_bytes must be a positive multiple of 1024");
+  if (num_tiles < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_tiles must be >= 0");
+  if (num_tiles == 0) return PA_OK;
+  if (!buf || !sink) return fail(PA_ERR_INVALID_ARGUMENT, "pointer arguments must not be NULL");
+  if (!aligned16(buf)) return fail(PA_ERR_INVALID_ARGUMENT, "buf must be 16-byte aligned");
+  const hipError_t e = pa::launch_read_probe(buf, tile_bytes, num_tiles, order, sink, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
 }  // extern "C"

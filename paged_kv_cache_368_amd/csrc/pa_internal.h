@@ -115,6 +115,10 @@ hipError_t launch_cache_write_fp8(const void *key, const void *value, void *key_
                                   int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                   int src_dt, float k_scale, float v_scale, hipStream_t stream);
 
+// Read-bandwidth probe (one uint32 of sink per work-group).
+hipError_t launch_read_probe(const void *buf, long long tile_bytes, long long num_tiles,
+                             const int32_t *order, uint32_t *sink, hipStream_t stream);
+
 hipError_t launch_compute_slots(int64_t *slot_mapping, const int32_t *block_tables,
                                 int max_blocks_per_seq, const int32_t *context_lens,
                                 const int32_t *seq_ids, const int32_t *positions,

@@ -217,3 +217,14 @@ def test_append_decode_fp8_rejects(lib):
     assert call(vs=float("inf")) == _capi.PA_ERR_INVALID_ARGUMENT
     assert call(value=_p(264)) == _capi.PA_ERR_INVALID_ARGUMENT
     assert call(S=0, out=None, q=None, key=None, value=None) == _capi.PA_OK
+
+
+def test_read_probe_rejects(lib):
+    rp = lib.pa_read_probe
+    assert rp(_p(), 1000, 8, None, _p(), None) == _capi.PA_ERR_INVALID_ARGUMENT     # not k*1024
+    assert rp(_p(), 0, 8, None, _p(), None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert rp(_p(), 4096, -1, None, _p(), None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert rp(None, 4096, 8, None, _p(), None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert rp(_p(), 4096, 8, None, None, None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert rp(_p(8), 4096, 8, None, _p(), None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert rp(None, 4096, 0, None, None, None) == _capi.PA_OK
