@@ -147,11 +147,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
 
   const int H = a.num_heads, S = a.num_seqs;
-#if PA_XCD_REMAP
-  const int item = xcd_logical_index(blockIdx.x, gridDim.x);
-#else
   const int item = blockIdx.x;
-#endif
   const int h = item % H;
   const int s = (item / H) % S;
   const int p = item / (H * S);

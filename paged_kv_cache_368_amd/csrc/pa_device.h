@@ -212,18 +212,6 @@ __device__ __forceinline__ float sum_xor32(float x) { float a, b; swap32(x, a, b
 __device__ __forceinline__ float max_xor16(float x) { float a, b; swap16(x, a, b); return fmaxf(a, b); }
 __device__ __forceinline__ float max_xor32(float x) { float a, b; swap32(x, a, b); return fmaxf(a, b); }
 
-// ---- work-group order --------------------------------------------------------
-
-// Work-groups are handed to the 8 XCDs round-robin by hardware id.  Return a
-// logical index such that consecutive logical indices run on the same XCD
-// (and so share its L2), while the hardware dispatch order is unchanged.
-__device__ __forceinline__ int xcd_logical_index(int hw_id, int n) {
-  constexpr int kXcd = 8;
-  const int per = n / kXcd, extra = n % kXcd;
-  const int x = hw_id % kXcd, k = hw_id / kXcd;
-  return x * per + (x < extra ? x : extra) + k;
-}
-
 // Word 3 of a raw (untyped, unswizzled) buffer descriptor on CDNA3/CDNA4.
 constexpr int kBufferFlags = 0x00020000;
 

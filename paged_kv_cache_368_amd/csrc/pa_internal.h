@@ -24,25 +24,13 @@ inline int elem_bytes(int dt) { return dt == kF32 ? 4 : dt == kFP8 ? 1 : 2; }
 // of the partition's table slice.
 constexpr int kMaxPartition = 4096;
 constexpr int kChunk = 16;            // tokens per inner-loop step of a wave
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 4
-#endif
-constexpr int kDecodeWaves = PA_DECODE_WAVES;   // waves per decode work-group
-#ifndef PA_XCD_REMAP
-#define PA_XCD_REMAP 0
-#endif
-#ifndef PA_DECODE_BUFFERS
-#define PA_DECODE_BUFFERS 2
-#endif
-constexpr int kDecodeBuffers = PA_DECODE_BUFFERS; // K/V chunk buffers in flight per wave
-#ifndef PA_DECODE_BUFFERS_FP8
-#define PA_DECODE_BUFFERS_FP8 2
-#endif
-constexpr int kDecodeBuffersFp8 = PA_DECODE_BUFFERS_FP8;  // the same for 8-bit pools
-#ifndef PA_GQA_WAVES
-#define PA_GQA_WAVES 4
-#endif
-constexpr int kGqaWaves = PA_GQA_WAVES;          // waves per grouped-query work-group
+// Work-group shapes and pipeline depths, each measured against its
+// neighbours on MI355X (more waves per decode work-group, or a third K/V
+// buffer, was no faster and cost occupancy).
+constexpr int kDecodeWaves = 4;       // waves per decode work-group
+constexpr int kDecodeBuffers = 2;     // K/V chunk buffers in flight per wave
+constexpr int kDecodeBuffersFp8 = 2;  // the same for 8-bit pools
+constexpr int kGqaWaves = 4;          // waves per grouped-query work-group
 constexpr int kMaxPartBlocks = kMaxPartition / 16;
 
 struct DecodeArgs {
