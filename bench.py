@@ -51,10 +51,21 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
     "llama7b_f16/B16/P4096/append": {
-        "sources": "08a26f9a88178f7a5fa0f89c8ff436c28f689ac57744589720941197cfe217b5",
-        "fetch_kib": 328580.438, "fetch_scale": 1048576 / 524299.500,
+        "sources": "7b9c17e20bf8cf79302e3fc321bba6087b615db9a1bff816547bb7fe1015be09",
+        "fetch_kib": 328580.625, "fetch_scale": 1048576 / 524300.500,
         "write_kib": 768.0, "write_scale": 1.0,
         "profile": "profiles/decode_mha_llama7b_f16.md"},
+    # decode_gqa_kernel + merge_kernel
+    "gqa70b_bf16/B16/P2048/append": {
+        "sources": "7b9c17e20bf8cf79302e3fc321bba6087b615db9a1bff816547bb7fe1015be09",
+        "fetch_kib": 103365.453 + 601.500, "fetch_scale": 1048576 / 524300.500,
+        "write_kib": 1104.062 + 256.0, "write_scale": 1.0,
+        "profile": "profiles/decode_gqa_gqa70b_bf16.md"},
+    "llama7b_fp8kv/B16/P4096/append": {
+        "sources": "7b9c17e20bf8cf79302e3fc321bba6087b615db9a1bff816547bb7fe1015be09",
+        "fetch_kib": 154698.984, "fetch_scale": 1048576 / 524300.500,
+        "write_kib": 512.0, "write_scale": 1.0,
+        "profile": "profiles/decode_fp8_llama7b_fp8kv.md"},
 }
 
 
