@@ -7,16 +7,17 @@
 // found through block_tables[s] (P3 §2-§3).  A prefix cached earlier (P3 §3,
 // shared prefixes save prefill work) is simply not among the queries.
 //
-// Work decomposition: one work-group of 4 waves per (sequence, 128-row query
+// Work decomposition: one work-group of 8 waves per (sequence, 256-row query
 // tile, query head); wave w owns rows 32w .. 32w+31 of the tile as two
 // 16-row subtiles, so each wave holds the complete softmax state of its rows
 // and no cross-wave merge is needed.  Every K and V operand read from LDS
 // feeds both subtiles' products, which halves the LDS traffic per flop
-// against one subtile per wave.  The work-group walks the context in
-// 32-token chunks that all four waves share:
+// against one subtile per wave, and each K/V chunk brought in serves 256
+// query rows, so the context is streamed once per 256 rows.  The work-group
+// walks the context in 32-token chunks that all eight waves share:
 //
 //   * K and V of a chunk go from HBM straight into LDS (buffer loads with
-//     the LDS bit: no registers), each wave moving a quarter of it, into one
+//     the LDS bit: no registers), the waves sharing the 1 KB loads, into one
 //     of two stages, so the next chunk streams in while this one is used.
 //     Rows are stored with their 16-byte pieces XOR-swizzled by the row index,
 //     which makes both operand reads below conflict-free.
@@ -41,7 +42,7 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyMax = 8.f;          // log2 units: weights stay <= 256
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 8;
 constexpr int kSub = 2;                  // 16-row subtiles per wave
 constexpr int kRows = 16 * kSub * kPfWaves;   // query rows per work-group
 constexpr int kCh = 32;                  // tokens per chunk
@@ -80,7 +81,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int ROW = D * E;                 // bytes per token row
   constexpr int PIECES = ROW / 16;           // 16-byte pieces per row
   constexpr int RPL = 1024 / ROW;            // rows per 1 KB wave load
-  constexpr int LPW = kCh * ROW / 1024 / kPfWaves;   // loads per wave per operand and chunk
+  constexpr int NLD = kCh * ROW / 1024;      // 1 KB loads per operand and chunk
+  constexpr int LPW = (NLD + kPfWaves - 1) / kPfWaves;   // of them per wave (at most)
   constexpr int KI = D / 32;                 // first-product steps
   constexpr int NT = D / 16;                 // output tiles of 16 dims
   constexpr int STAGE = kCh * ROW;           // bytes of one operand in one stage
@@ -217,7 +219,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
       const int tc = w0 + k * kCh;
 #pragma unroll
       for (int jj = 0; jj < LPW; ++jj) {
-        const int j = wave * LPW + jj;                   // 1 KB load index within the chunk
+        const int j = wave + kPfWaves * jj;              // 1 KB load index within the chunk
+        if (j >= NLD) break;                             // uniform
         const int trow0 = tc + j * RPL;                  // first token of the load
         const bool any = trow0 < wend;
         const int phys =
