@@ -25,21 +25,21 @@
 // end with the same max-rescaled sums.
 //
 // Pipelining.  K and V of chunk k+1 are issued before chunk k is consumed
-// (double-buffered registers), the in-kernel form of P1 §4's "load the next
-// block while computing the current one".
+// (double-buffered registers): P1 §4's overlap of the next block's loads with
+// the current block's arithmetic, kept inside the kernel.
 //
 // Masking.  Tokens past the context in the last chunk get score -inf and
 // their V words are zeroed by select, so whatever the unused slots hold
 // (NaN in the tests) never reaches the result.
 //
-// Appending decode (pa_append_decode, pools of the query's type): the newest
-// token of each sequence (position context_lens - 1) arrives as an input row.
-// The row is loaded with q and kept in LDS; the partition that holds the
-// token streams the pool only up to the token before it (whatever the slot
-// held before never counts) and takes the new row as one extra masked chunk
-// after its loop, and one work-group per (sequence, kv head) stores it into
-// the slot for later steps: the slot resolution, the cache write and the
-// attention of a decode step in one launch.
+// Appending decode (pa_append_decode, pa_append_decode_fp8): the newest
+// token of each sequence (position context_lens - 1) arrives as an input row
+// (quantised here for E4M3 pools).  The row is kept in LDS; the partition
+// that holds the token streams the pool only up to the token before it
+// (whatever the slot held before never counts) and takes the new row as one
+// extra masked chunk after its loop, and one work-group per (sequence, kv
+// head) stores it into the slot for later steps: the slot resolution, the
+// cache write and the attention of a decode step in one launch.
 #include "pa_device.h"
 
 namespace pa {
