@@ -13,7 +13,8 @@ context_lens over a step / step time) with every input already in HBM.
 ``roofline`` rates the decode launch: algorithmic bytes (K and V of every
 context token, q, out, and the used block-table entries) over its mean
 duration, measured with HIP events on the stream the kernels run on (around
-every fifth timed step's call), against the MI355X HBM peak of 8 TB/s.  ``cpu_baseline`` times the float64 oracle on
+runs of five timed steps, or every fifth decode call of the three-call
+step), against the MI355X HBM peak of 8 TB/s.  ``cpu_baseline`` times the float64 oracle on
 a bounded sample of the same workload on this host.
 
 Pools are rotated between steps (several resident copies, each larger than
@@ -508,20 +509,36 @@ def main(argv=None) -> int:
         step(i)
     torch.cuda.synchronize()
 
-    # HIP events bracket the decode call of every EVENT_EVERY-th timed step
-    # (every step when there are fewer than 2 * EVENT_EVERY): an event pair
-    # on every step adds ~8 us to a ~105 us LLaMA-7B step, which is the
-    # instrument's cost, not the step's.
+    # Launch durations from HIP events on the kernels' stream.  One-launch
+    # steps: an event pair brackets each run of EVENT_EVERY consecutive steps
+    # (launch duration = elapsed / run length), so the events' own cost (~8 us
+    # per pair on a ~105 us LLaMA-7B step) is paid once per run.  Three-call
+    # steps: the pair brackets the decode call of every EVENT_EVERY-th step.
+    # Fewer than 2 * EVENT_EVERY timed steps: every step is measured alone.
     every = EVENT_EVERY if args.steps >= 2 * EVENT_EVERY else 1
-    events = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for i in range(0, args.steps, every)}
+    samples = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, events.get(i))
+    if fused:
+        for g0 in range(0, args.steps, every):
+            g1 = min(g0 + every, args.steps)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(g0, g1):
+                step(args.warmup + i)
+            e1.record(stream)
+            samples.append((e0, e1, g1 - g0))
+    else:
+        for i in range(args.steps):
+            if i % every == 0:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                samples.append((ev[0], ev[1], 1))
+                step(args.warmup + i, ev)
+            else:
+                step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = sorted(e[0].elapsed_time(e[1]) for e in events.values())
+    dec_ms = sorted(e0.elapsed_time(e1) / n for e0, e1, n in samples)
     dec_mean_s = sum(dec_ms) / len(dec_ms) / 1e3
     dec_med_s = dec_ms[len(dec_ms) // 2] / 1e3
     print(f"[bench] {args.steps} steps in {wall * 1e3:.2f} ms; decode mean {dec_mean_s * 1e6:.1f} us "
@@ -590,7 +607,8 @@ def main(argv=None) -> int:
                                ("_fp8" if fp8 else "") +
                                " (decode kernel + merge pass when split)",
                      "bytes_per_launch": nbytes["total"], "mean_launch_us": dec_mean_s * 1e6,
-                     "median_launch_us": dec_med_s * 1e6, "timed_launches": len(dec_ms),
+                     "median_launch_us": dec_med_s * 1e6, "event_samples": len(dec_ms),
+                     "launches_per_sample": every if fused else 1,
                      "p10_launch_us": dec_ms[len(dec_ms) // 10] * 1e3,
                      "p90_launch_us": dec_ms[(9 * len(dec_ms)) // 10] * 1e3},
         "read_ceiling": ceiling,
