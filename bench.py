@@ -400,7 +400,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1,
-                    help="workload index 0..5 (default 1: LLaMA-7B shape; 5: the same with fp8 K/V)")
+                    help="workload index 0..6 (default 1: LLaMA-7B shape; 5 and 6: the LLaMA-7B "
+                         "and 70B-style GQA shapes with fp8 K/V)")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--seed", type=int, default=None)

@@ -288,13 +288,14 @@ CONFIG_NAMES = {
     3: "gqa70b_bf16",
     4: "longctx_prefix_f16",
     5: "llama7b_fp8kv",
+    6: "gqa70b_fp8kv",
 }
 
 
 def make_workload(index: int, seed: int | None = None, block_size: int | None = None,
                   num_seqs: int | None = None, head_scale: int = 1,
                   ctx_override=None) -> Workload:
-    """Workload ``index`` (0..5).  ``seed`` defaults to the index.
+    """Workload ``index`` (0..6).  ``seed`` defaults to the index.
 
     ``num_seqs`` / ``head_scale`` (divide head counts by it) / ``ctx_override``
     shrink a workload for oracle-sized parity runs without changing its
@@ -339,6 +340,13 @@ def make_workload(index: int, seed: int | None = None, block_size: int | None = 
         return build(name, "f16", ctx, 32 // head_scale, 32 // head_scale, 128, block_size or 16, seed,
                      pool="choice", pool_factor=1.2, value_scale=0.5, kv_dtype="fp8",
                      kv_scale=0.5)
+    if index == 6:
+        # The 70B-style grouped-query share with 8-bit (E4M3) K/V pools, scale
+        # 0.5: bf16 queries and outputs over 8 kv heads of 8 query heads each.
+        S = num_seqs or 16
+        ctx = rng.integers(2048, 4096 + 1, size=S) if ctx_override is None else ctx_override
+        return build(name, "bf16", ctx, 64 // head_scale, 8 // head_scale, 128, block_size or 16,
+                     seed, pool="permutation", kv_dtype="fp8", kv_scale=0.5)
     raise ValueError(index)
 
 
