@@ -1,5 +1,6 @@
 // PagedAttention decode for grouped-query attention on the matrix cores
-// (gfx950), fp16 and bf16.
+// (gfx950): fp16 and bf16 queries over pools of the same type or of E4M3
+// codes with per-pool scales.
 //
 // Same result as the vector kernel (P1 §1 first formula over the context
 // gathered through the block table, P3 §2-§3), but the G query heads that
@@ -36,10 +37,17 @@
 // from fp32 or bf16 limits, and the final o/l is independent of the
 // reference chosen.
 //
+// E4M3 pools: each lane widens the 16 codes it loaded to 16 values of the
+// query's type (exact) as it writes them to the LDS tile, so the tiles, the
+// products and the softmax are those of the 16-bit path.  The K pool scale is
+// folded into the score scale and the V pool scale is applied to the
+// accumulated output.
+//
 // Appending decode: the newest token's K/V rows come from the input (staged in
-// LDS by the prologue and written over the pool's row in the chunk's LDS
-// tiles, so whatever the slot held before never counts), and the work-group
-// of the partition holding the token stores them into its slot.
+// LDS by the prologue, as pool rows: quantised first for E4M3 pools, and
+// written over the pool's row in the chunk's LDS tiles, so whatever the slot
+// held before never counts), and the work-group of the partition holding the
+// token stores them into its slot.
 #include "pa_mfma.h"
 
 namespace pa {
@@ -50,23 +58,44 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyMax = 8.f;          // log2 units: weights stay <= 256
 constexpr int kGMax = 16;                // query heads per kv head on one tile
 
+// Stage one 16-byte pool load (lane column col of a token row) in an LDS
+// tile row of 16-bit values: as it is, or widened from 16 E4M3 codes to 32
+// bytes of the query's type.
+template <int DT, int KT>
+__device__ __forceinline__ void stage16(unsigned char *row, int col, const u32x4 &w) {
+  if constexpr (KT == kFP8) {
+    const u32x4 lo = {fp8_pair<DT, false>(w.x), fp8_pair<DT, true>(w.x),
+                      fp8_pair<DT, false>(w.y), fp8_pair<DT, true>(w.y)};
+    const u32x4 hi = {fp8_pair<DT, false>(w.z), fp8_pair<DT, true>(w.z),
+                      fp8_pair<DT, false>(w.w), fp8_pair<DT, true>(w.w)};
+    *reinterpret_cast<u32x4 *>(row + 32 * col) = lo;
+    *reinterpret_cast<u32x4 *>(row + 32 * col + 16) = hi;
+  } else {
+    *reinterpret_cast<u32x4 *>(row + 16 * col) = w;
+  }
+}
+
 // Three waves per SIMD fit without spilling at head_dim 128 (153 VGPRs).
-template <int DT, int D, int NW>
+template <int DT, int KT, int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_gqa_kernel(DecodeArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(NW * 64 >= kMaxPartBlocks, "one thread per staged block id");
-  constexpr int E = 2;
-  constexpr int ROW = D * E;                 // bytes per token row
+  static_assert(KT == DT || KT == kFP8, "pool type");
+  constexpr bool kF8 = KT == kFP8;
+  constexpr int E = 2;                       // bytes per element of q, out and the tiles
+  constexpr int EKV = kF8 ? 1 : 2;           // bytes per element of the pools
+  constexpr int ROW = D * E;                 // bytes per token row of q and of a tile
+  constexpr int ROWKV = D * EKV;             // bytes per token row in the pools
   constexpr int PITCH = ROW + 32;            // LDS row pitch: 16-byte rows, spread banks
   constexpr int KI = D / 32;                 // first-product steps
   constexpr int NT = D / 16;                 // output tiles of 16 dims
-  constexpr int LPT = ROW / 16;              // lanes per row for the V loads
-  constexpr int TPL = 64 / LPT;              // rows per V wave load
-  constexpr int VL = kChunk / TPL;           // V loads per chunk
+  constexpr int LPT = ROWKV / 16;            // lanes per pool row for the K/V loads
+  constexpr int TPL = 64 / LPT;              // rows per K/V wave load
+  constexpr int VL = kChunk / TPL;           // K/V loads per chunk
 
   __shared__ int s_tbl[kMaxPartBlocks];
-  __shared__ u32x4 s_new[2][ROW / 16];      // the newest token's K and V rows (appending)
+  __shared__ u32x4 s_new[2][LPT];           // the newest token's K and V pool rows (appending)
   // K and V tiles (one pair per wave) during the loop; reused for the
   // cross-wave merge afterwards.
   constexpr int kTileBytes = kChunk * PITCH;
@@ -101,10 +130,27 @@ void decode_gqa_kernel(DecodeArgs a) {
   // of the chunk), lane l reads row (l/LPT) + TPL*j, bytes 16*(l%LPT).
   const int v_row = lane / LPT, v_col = lane % LPT;
   const bool append = a.new_k != nullptr;                  // uniform (kernel argument)
-  // Lanes 0..LPT-1 (wave 0, row 0) hold the newest token's rows.
+  // Lanes 0..LPT-1 (wave 0, row 0) write the newest token's pool rows.
   const bool new_lane = append && tid < LPT;
   u32x4 nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
-  if (new_lane) {
+  if constexpr (kF8) {
+    // Quantised as the separate cache write does, four elements per lane
+    // over wave 0 (K on lanes 0..D/4-1, V on the next D/4).
+    constexpr int NE = D / 4;
+    if (append && tid < 2 * NE) {
+      const bool isv = tid >= NE;
+      const int w = isv ? tid - NE : tid;
+      const u32x2 raw = *reinterpret_cast<const u32x2 *>(
+          static_cast<const char *>(isv ? a.new_v : a.new_k) +
+          ((size_t)s * Hkv + kvh) * ROW + 8 * w);
+      const float sc = isv ? a.v_scale : a.k_scale;
+      const uint32_t word = e4m3_code(lo_f32<DT>(raw.x) / sc) |
+                            (e4m3_code(hi_f32<DT>(raw.x) / sc) << 8) |
+                            (e4m3_code(lo_f32<DT>(raw.y) / sc) << 16) |
+                            (e4m3_code(hi_f32<DT>(raw.y) / sc) << 24);
+      reinterpret_cast<uint32_t *>(&s_new[isv ? 1 : 0][0])[w] = word;
+    }
+  } else if (new_lane) {
     const size_t new_off = ((size_t)s * Hkv + kvh) * ROW + 16 * v_col;
     nk = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.new_k) + new_off);
     nv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.new_v) + new_off);
@@ -144,7 +190,11 @@ void decode_gqa_kernel(DecodeArgs a) {
     const int phys = s_tbl[(tn - t0) >> a.log2_block];
     if (phys >= 0 && phys < a.num_blocks) {
       const size_t dst = ((size_t)phys * block_stride + kvh * head_stride +
-                          (size_t)(tn & (a.block_size - 1)) * D) * E + 16 * v_col;
+                          (size_t)(tn & (a.block_size - 1)) * D) * EKV + 16 * v_col;
+      if constexpr (kF8) {            // the codes, staged before the barrier above
+        nk = s_new[0][v_col];
+        nv = s_new[1][v_col];
+      }
       *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_store) + dst) = nk;
       *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_store) + dst) = nv;
     }
@@ -175,17 +225,17 @@ void decode_gqa_kernel(DecodeArgs a) {
   if (lane < nch_w) my_ids = s_tbl[((wave + NW * lane) * kChunk) >> a.log2_block];
 
   const char *kbase =
-      scalar_ptr(reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E);
+      scalar_ptr(reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * EKV);
   const char *vbase =
-      scalar_ptr(reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E);
-  const int v_off = v_row * ROW + 16 * v_col;
-  constexpr int kChunkBytes = kChunk * ROW;
+      scalar_ptr(reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * EKV);
+  const int v_off = v_row * ROWKV + 16 * v_col;
+  constexpr int kChunkBytes = kChunk * ROWKV;
 
   auto chunk_offset = [&](int k) -> size_t {
     const int phys = __builtin_amdgcn_readlane(my_ids, k);
     const int tok = (wave + NW * k) * kChunk;
     const int off = tok & (a.block_size - 1);
-    return ((size_t)phys * block_stride + (size_t)off * D) * E;
+    return ((size_t)phys * block_stride + (size_t)off * D) * EKV;
   };
   // Chunks past the wave's last one (the pipeline's run-out) are loaded
   // through an empty descriptor: such loads return zeros without touching
@@ -199,10 +249,10 @@ void decode_gqa_kernel(DecodeArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, range, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < VL; ++j)
-      kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, v_off + j * TPL * ROW, 0, kStreamPolicy);
+      kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, v_off + j * TPL * ROWKV, 0, kStreamPolicy);
 #pragma unroll
     for (int j = 0; j < VL; ++j)
-      vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, v_off + j * TPL * ROW, 0, kStreamPolicy);
+      vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, v_off + j * TPL * ROWKV, 0, kStreamPolicy);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -230,10 +280,8 @@ void decode_gqa_kernel(DecodeArgs a) {
     // bytes 64i + 16*(l/16) of its row).  Rows past the context are left as
     // they are: their scores are replaced by -inf below, by select.
 #pragma unroll
-    for (int j = 0; j < VL; ++j)
-      *reinterpret_cast<u32x4 *>(ktile + (v_row + j * TPL) * PITCH + 16 * v_col) = kb[j];
-    if (inject && lane < LPT)
-      *reinterpret_cast<u32x4 *>(ktile + rn * PITCH + 16 * lane) = s_new[0][lane];
+    for (int j = 0; j < VL; ++j) stage16<DT, KT>(ktile + (v_row + j * TPL) * PITCH, v_col, kb[j]);
+    if (inject && lane < LPT) stage16<DT, KT>(ktile + rn * PITCH, lane, s_new[0][lane]);
     u32x4 ka[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i)
@@ -260,10 +308,8 @@ void decode_gqa_kernel(DecodeArgs a) {
     }
     // V: stage the chunk in this wave's LDS tile.
 #pragma unroll
-    for (int j = 0; j < VL; ++j)
-      *reinterpret_cast<u32x4 *>(tile + (v_row + j * TPL) * PITCH + 16 * v_col) = vr[j];
-    if (inject && lane < LPT)
-      *reinterpret_cast<u32x4 *>(tile + rn * PITCH + 16 * lane) = s_new[1][lane];
+    for (int j = 0; j < VL; ++j) stage16<DT, KT>(tile + (v_row + j * TPL) * PITCH, v_col, vr[j]);
+    if (inject && lane < LPT) stage16<DT, KT>(tile + rn * PITCH, lane, s_new[1][lane]);
 
     // Raise the reference only when some score exceeds it by kLazyMax: every
     // lane of a query column holds the column's m, so the test needs no
@@ -355,6 +401,7 @@ void decode_gqa_kernel(DecodeArgs a) {
       L += f * s_l[w * kGMax + q];
       O += f * s_o[(w * kGMax + q) * D + d];
     }
+    if constexpr (kF8) O *= a.v_scale;        // the tiles held V codes
     const int h = kvh * G + q;
     if (direct) {
       const float r = L == 0.f ? 0.f : O / L;
@@ -370,29 +417,35 @@ void decode_gqa_kernel(DecodeArgs a) {
   }
 }
 
-template <int DT, int D>
+template <int DT, int KT, int D>
 hipError_t launch_gqa_t(const DecodeArgs &a, hipStream_t stream) {
   const long n = (long)a.num_seqs * a.num_kv_heads * a.num_partitions;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_gqa_kernel<DT, D, kGqaWaves>), dim3((unsigned)n), dim3(kGqaWaves * 64),
-                     0, stream, a);
+  hipLaunchKernelGGL((decode_gqa_kernel<DT, KT, D, kGqaWaves>), dim3((unsigned)n),
+                     dim3(kGqaWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool gqa_supported(int dt, int head_dim, int num_heads, int num_kv_heads) {
+bool gqa_supported(int kv_dt, int head_dim, int num_heads, int num_kv_heads) {
   const int G = num_heads / num_kv_heads;
-  return (dt == kF16 || dt == kBF16) && (head_dim == 64 || head_dim == 128) && G >= 2 &&
-         G <= kGMax;
+  return (kv_dt == kF16 || kv_dt == kBF16 || kv_dt == kFP8) &&
+         (head_dim == 64 || head_dim == 128) && G >= 2 && G <= kGMax;
 }
 
-hipError_t launch_decode_gqa(const DecodeArgs &a, int dt, hipStream_t stream) {
-  switch (dt * 1000 + a.head_dim) {
-    case kF16 * 1000 + 64: return launch_gqa_t<kF16, 64>(a, stream);
-    case kF16 * 1000 + 128: return launch_gqa_t<kF16, 128>(a, stream);
-    case kBF16 * 1000 + 64: return launch_gqa_t<kBF16, 64>(a, stream);
-    case kBF16 * 1000 + 128: return launch_gqa_t<kBF16, 128>(a, stream);
+hipError_t launch_decode_gqa(const DecodeArgs &a, int dt, int kv_dt, hipStream_t stream) {
+  const bool f8 = kv_dt == kFP8;
+  if (!f8 && kv_dt != dt) return hipErrorInvalidValue;
+  switch ((f8 ? 10000 : 0) + dt * 1000 + a.head_dim) {
+    case kF16 * 1000 + 64: return launch_gqa_t<kF16, kF16, 64>(a, stream);
+    case kF16 * 1000 + 128: return launch_gqa_t<kF16, kF16, 128>(a, stream);
+    case kBF16 * 1000 + 64: return launch_gqa_t<kBF16, kBF16, 64>(a, stream);
+    case kBF16 * 1000 + 128: return launch_gqa_t<kBF16, kBF16, 128>(a, stream);
+    case 10000 + kF16 * 1000 + 64: return launch_gqa_t<kF16, kFP8, 64>(a, stream);
+    case 10000 + kF16 * 1000 + 128: return launch_gqa_t<kF16, kFP8, 128>(a, stream);
+    case 10000 + kBF16 * 1000 + 64: return launch_gqa_t<kBF16, kFP8, 64>(a, stream);
+    case 10000 + kBF16 * 1000 + 128: return launch_gqa_t<kBF16, kFP8, 128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -58,16 +58,6 @@ struct MhaShape {
   static_assert(kLpt == 4 || kLpt == 8 || kLpt == 16 || kLpt == 32, "row width");
 };
 
-// Two E4M3 codes (bytes 0-1 or 2-3 of a word) as a packed 16-bit pair of the
-// query's type; exact (every E4M3 value is a binary16 and a bfloat16 value).
-template <int QT, bool HI>
-__device__ __forceinline__ uint32_t fp8_pair(uint32_t w) {
-  if constexpr (QT == kBF16)
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-  else
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
-}
-
 // Per-lane dot of the lane's slice of q and of a K row: 16 bytes of K, and
 // q in its own type (16 bytes, or 32 bytes against 16 E4M3 codes).
 template <int QT, int KT>

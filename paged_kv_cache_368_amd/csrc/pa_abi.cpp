@@ -102,8 +102,11 @@ pa_status_t plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
     // (sequence, kv head) on the matrix-core grouped-query kernel.
     const bool gqa = pa::gqa_supported(dtype, head_dim, num_heads, num_kv_heads);
     const long long items = (long long)num_seqs * (gqa ? num_kv_heads : num_heads);
+    // The matrix-core kernel does the same per-token work over E4M3 pools
+    // for half the bytes: it was measured fastest with two work-groups per CU.
+    const long long min_wg = gqa && dtype == PA_FP8_E4M3 ? 2 * kMinWorkgroups : kMinWorkgroups;
     P = max_context_len > pa::kMaxPartition ? pa::kMaxPartition / 2 : pa::kMaxPartition;
-    while (P > 256 && items * ceil_div(max_context_len, P) < kMinWorkgroups) P /= 2;
+    while (P > 256 && items * ceil_div(max_context_len, P) < min_wg) P /= 2;
   }
   const long long np = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
   if ((long long)num_seqs * num_heads * np > 0x7fffffffLL)
@@ -310,8 +313,8 @@ pa_status_t decode_impl(void *out, const void *q, const void *key_cache, const v
   a.k_store = const_cast<void *>(key_cache);
   a.v_store = const_cast<void *>(value_cache);
 
-  hipError_t e = kv_dt == q_dt && pa::gqa_supported(q_dt, head_dim, num_heads, num_kv_heads)
-                     ? pa::launch_decode_gqa(a, q_dt, stream)
+  hipError_t e = pa::gqa_supported(kv_dt, head_dim, num_heads, num_kv_heads)
+                     ? pa::launch_decode_gqa(a, q_dt, kv_dt, stream)
                      : pa::launch_decode_mha(a, q_dt, kv_dt, stream);
   if (e == hipSuccess && z.num_partitions > 1) e = pa::launch_merge(a, q_dt, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));

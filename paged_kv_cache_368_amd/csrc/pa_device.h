@@ -57,6 +57,16 @@ template <> __device__ __forceinline__ float dot2<kBF16>(uint32_t a, uint32_t b,
                                          __builtin_bit_cast(bf16x2, b), acc, false);
 }
 
+// Two E4M3 codes (bytes 0-1 or 2-3 of a word) as a packed 16-bit pair of a
+// 16-bit type QT; exact (every E4M3 value is a binary16 and a bfloat16 value).
+template <int QT, bool HI>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w) {
+  if constexpr (QT == kBF16)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
 // Round float32 to the storage type, nearest-even; returns the storage bits.
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;

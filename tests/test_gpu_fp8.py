@@ -77,12 +77,14 @@ def test_cache_write_fp8_bitexact(src):
 
 
 @pytest.mark.parametrize("qt", ["f16", "bf16"])
-def test_context_one_returns_every_code_exactly(qt):
+@pytest.mark.parametrize("H", [2, 8])
+def test_context_one_returns_every_code_exactly(qt, H):
     """One token whose V rows hold every finite E4M3 code: the output is
     exactly code * v_scale (a power of two keeps it exact in the output
-    type)."""
-    _say(f"fp8 ctx=1 all codes {qt}")
-    Hkv, H, B, D = 2, 2, 16, 128
+    type), on the vector kernel (one query head per kv head) and on the
+    matrix-core kernel (four)."""
+    _say(f"fp8 ctx=1 all codes {qt} H={H}")
+    Hkv, B, D = 2, 16, 128
     finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # 254 codes
     row = np.concatenate([finite, finite[:2 * D - len(finite)]]).reshape(Hkv, D)
     kc = e4m3_codes(3, 1, (4, Hkv, B, D))
@@ -94,7 +96,7 @@ def test_context_one_returns_every_code_exactly(qt):
     wl.key_cache, wl.value_cache, wl.q = kc, vc, q
     wl.block_tables[:] = 2
     got = _fp8_decode(wl)
-    want = P.e4m3_decode(row) * 0.25
+    want = np.repeat(P.e4m3_decode(row) * 0.25, H // Hkv, axis=0)
     assert np.array_equal(got[0], want), np.argwhere(got[0] != want)[:4]
 
 
@@ -103,6 +105,9 @@ FP8_CASES = [
     ("mha_d64_b32", dict(ctx=[64, 200, 31], H=4, Hkv=4, D=64, B=32)),
     ("gqa_g4_b64", dict(ctx=[300, 1, 129], H=8, Hkv=2, D=128, B=64)),
     ("gqa_g8_d64", dict(ctx=[77, 512], H=16, Hkv=2, D=64, B=16)),
+    ("gqa_g16_d128", dict(ctx=[1, 16, 17, 250, 1030], H=32, Hkv=2, D=128, B=16)),
+    ("gqa_g2_d64_b32", dict(ctx=[2, 31, 33, 600], H=4, Hkv=2, D=64, B=32)),
+    ("gqa_g5_d128", dict(ctx=[45, 700], H=10, Hkv=2, D=128, B=16)),
 ]
 
 
@@ -129,18 +134,20 @@ def test_decode_fp8_invalid_values_poison_only_their_row():
     BD.assert_close(got[[0, 2]], ref[[0, 2]], "f16", "good rows")
 
 
-def test_decode_fp8_full_size_sampled():
-    """The LLaMA-7B-shaped fp8 workload at full size, in the bench's launch
-    configuration; outputs checked on a sample of (sequence, head) rows."""
-    _say("fp8 full-size llama7b sampled")
-    wl = make_workload(5)
-    got = _fp8_decode(wl)
+@pytest.mark.parametrize("idx", [5, 6])
+def test_decode_fp8_full_size_sampled(idx):
+    """The LLaMA-7B-shaped and the 70B-style grouped-query fp8 workloads at
+    full size, in the bench's launch configuration; outputs checked on a
+    sample of (sequence, head) rows."""
+    _say(f"fp8 full-size config {idx} sampled")
+    wl = make_workload(idx)
+    got = _fp8_decode(wl, partition_size=wl.partition_size)
     rng = np.random.default_rng(0)
     pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, wl.num_seqs, 24),
                                                 rng.integers(0, wl.num_heads, 24))]
     ref = _oracle(wl, pairs=pairs)
-    idx = tuple(np.array(pairs).T)
-    BD.assert_close(got[idx], ref[idx], "f16", "llama7b fp8 sample")
+    sel = tuple(np.array(pairs).T)
+    BD.assert_close(got[sel], ref[sel], wl.dtype, "fp8 sample")
     assert np.isfinite(got).all()
 
 
