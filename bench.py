@@ -53,21 +53,27 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
     "llama7b_f16/B16/P4096/append": {
-        "sources": "71f275e84e2320571cdf19ef7cab00fd03ccd653bb8ee243fac78fe27243f0f2",
-        "fetch_kib": 328580.625, "fetch_scale": 1048576 / 524300.500,
+        "sources": "fc88b16c18b2330fc9b33976e7dd8012cbec99c9e7f3725a6c5c74bf2fcf9ef3",
+        "fetch_kib": 328576.469, "fetch_scale": 1048576 / 524300.500,
         "write_kib": 768.0, "write_scale": 1.0,
         "profile": "profiles/decode_mha_llama7b_f16.md"},
     # decode_gqa_kernel + merge_kernel
     "gqa70b_bf16/B16/P2048/append": {
-        "sources": "71f275e84e2320571cdf19ef7cab00fd03ccd653bb8ee243fac78fe27243f0f2",
-        "fetch_kib": 103365.453 + 601.500, "fetch_scale": 1048576 / 524300.500,
-        "write_kib": 1104.062 + 256.0, "write_scale": 1.0,
+        "sources": "fc88b16c18b2330fc9b33976e7dd8012cbec99c9e7f3725a6c5c74bf2fcf9ef3",
+        "fetch_kib": 103365.078 + 601.500, "fetch_scale": 1048576 / 524300.500,
+        "write_kib": 1104.188 + 256.0, "write_scale": 1.0,
         "profile": "profiles/decode_gqa_gqa70b_bf16.md"},
     "llama7b_fp8kv/B16/P4096/append": {
-        "sources": "71f275e84e2320571cdf19ef7cab00fd03ccd653bb8ee243fac78fe27243f0f2",
-        "fetch_kib": 154698.984, "fetch_scale": 1048576 / 524300.500,
+        "sources": "fc88b16c18b2330fc9b33976e7dd8012cbec99c9e7f3725a6c5c74bf2fcf9ef3",
+        "fetch_kib": 154700.328, "fetch_scale": 1048576 / 524300.500,
         "write_kib": 512.0, "write_scale": 1.0,
         "profile": "profiles/decode_fp8_llama7b_fp8kv.md"},
+    # decode_gqa_kernel over E4M3 pools + merge_kernel
+    "gqa70b_fp8kv/B16/P1024/append": {
+        "sources": "fc88b16c18b2330fc9b33976e7dd8012cbec99c9e7f3725a6c5c74bf2fcf9ef3",
+        "fetch_kib": 49054.250 + 969.500, "fetch_scale": 1048576 / 524300.500,
+        "write_kib": 1824.031 + 256.0, "write_scale": 1.0,
+        "profile": "profiles/decode_gqa_fp8_gqa70b_fp8kv.md"},
 }
 
 
