@@ -75,6 +75,17 @@ def test_prefill_matches_oracle(name, kw, dtype):
     BD.assert_close(got, _oracle(wl, qs, q), dtype, name)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.125, 2.0])
+def test_prefill_other_scales(scale):
+    """A zero scale (equal weights over each row's causal window: masked
+    tokens must still count zero), a negative one and a large one."""
+    _say(f"prefill scale {scale}")
+    wl, qs, q = _case("f16", [40, 77, 16], [40, 30, 16], 2, 2, 128, 16, seed=14)
+    wl.scale = scale
+    got = _run(wl, qs, q)
+    BD.assert_close(got, _oracle(wl, qs, q), "f16", f"scale {scale}")
+
+
 def test_prefill_crosses_table_windows():
     """Contexts longer than one staged window of block ids (4096 tokens)."""
     _say("prefill long contexts across windows")
