@@ -330,3 +330,20 @@ def test_decode_split_ignores_workspace_contents(dtype, H, Hkv):
             if first is None:
                 first = got
             assert np.array_equal(got, first), f"{fill}: output differs from the first call"
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 1.5])
+@pytest.mark.parametrize("dtype,H,Hkv", [("f16", 4, 4), ("bf16", 16, 2), ("f32", 4, 2)])
+def test_decode_other_scales(scale, dtype, H, Hkv):
+    """A zero scale (equal weights: the mean of V over the context, tail
+    slots of the last block excluded), a negative one and a large one, on
+    the vector kernel and the matrix-core kernel, one and several
+    partitions."""
+    wl = build("scales", dtype, [1, 17, 300, 1030], H, Hkv, 128, 16, seed=62, pool="choice",
+               pool_factor=1.3)
+    wl.scale = scale
+    ref = _oracle(wl)
+    for ps in (0, 64):
+        _say(f"decode scale {scale} {dtype} H={H}/{Hkv} P={ps}")
+        got = _run_decode(wl, ps)
+        _assert_close(got, ref, dtype, f"scale {scale} {dtype} P={ps}")
