@@ -561,20 +561,30 @@ def main(argv=None) -> int:
         sink = torch.empty(pa.PA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
         perm = torch.randperm(big.numel() * 4 // 4096, device="cuda",
                               generator=torch.Generator(device="cuda").manual_seed(0)).int()
-        ceiling = {"how": "pa_read_probe over 2 GiB, best of 5 HIP-event-timed calls"}
-        for key, order in (("contiguous_gbps", None), ("random_4k_tiles_gbps", perm)):
-            pa.pa_read_probe(big, 4096, order, sink)
+        # Also 4 KB tiles in random order over as many bytes as the call's K
+        # and V (a shorter read pays its ramp-up and tail on fewer bytes).
+        n_same = max(1, min(nbytes["kv"] // 4096, perm.numel()))
+        perm_same = torch.randperm(n_same, device="cuda",
+                                   generator=torch.Generator(device="cuda").manual_seed(1)).int()
+        ceiling = {"how": "pa_read_probe, best of 5 HIP-event-timed calls: 2 GiB in index "
+                          "order, 2 GiB as random 4 KB tiles, the call's K+V bytes as random "
+                          "4 KB tiles"}
+        for key, buf, order in (("contiguous_gbps", big, None),
+                                ("random_4k_tiles_gbps", big, perm),
+                                ("random_4k_tiles_same_bytes_gbps", big[:n_same * 1024],
+                                 perm_same)):
+            pa.pa_read_probe(buf, 4096, order, sink)
             best = float("inf")
             for _ in range(5):
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                pa.pa_read_probe(big, 4096, order, sink)
+                pa.pa_read_probe(buf, 4096, order, sink)
                 e1.record(stream)
                 torch.cuda.synchronize()
                 best = min(best, e0.elapsed_time(e1) / 1e3)
-            ceiling[key] = big.numel() * 4 / best / 1e9
-        del big, perm, sink
+            ceiling[key] = buf.numel() * 4 / best / 1e9
+        del big, perm, perm_same, sink
         torch.cuda.synchronize()
 
     if args.copy_calibration_mib:
@@ -620,6 +630,8 @@ def main(argv=None) -> int:
                      "p90_launch_us": dec_ms[(9 * len(dec_ms)) // 10] * 1e3},
         "read_ceiling": ceiling,
         "frac_of_tile_ceiling": (achieved / ceiling["random_4k_tiles_gbps"]) if ceiling else None,
+        "frac_of_same_bytes_tile_ceiling":
+            (achieved / ceiling["random_4k_tiles_same_bytes_gbps"]) if ceiling else None,
         "decode_context_tokens_per_s": sum_ctx / dec_mean_s,
         "device": dev_name,
     }
