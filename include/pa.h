@@ -301,8 +301,9 @@ pa_status_t pa_cache_write_fp8(const void *key, const void *value, void *key_cac
  * values code * k_scale (keys) and code * v_scale (values); q and out are
  * fp16 or bf16 (q_dtype), arithmetic is float32.  Every other argument,
  * the partition and workspace rules (size them with dtype PA_FP8_E4M3) and
- * the handling of invalid device values are those of pa_decode.  Runs on the
- * vector units for every head grouping.
+ * the handling of invalid device values are those of pa_decode.  With
+ * 2 <= num_heads / num_kv_heads <= 16 it runs on the matrix cores (the codes
+ * widened exactly to q's type), otherwise on the vector units.
  */
 pa_status_t pa_decode_fp8(void *out, const void *q, const void *key_cache,
                           const void *value_cache, const int32_t *block_tables,
