@@ -308,6 +308,81 @@ def _copy_cpu_baseline(Hkv, B, D, npairs) -> dict:
             "sample": f"{done} of {npairs} block pairs (K and V), numpy, 1 thread on {_cpu_name()}"}
 
 
+def bench_cache_write(args) -> dict:
+    """pa_cache_write on LLaMA-13B-shaped bf16 pools (8192 blocks of 16
+    tokens, 40 kv heads of 128): the K/V rows of a prompt batch (8 x 2048
+    tokens, the value: GB/s of rows read + slot bytes written) and of one
+    decode step (64 tokens, latency), each into distinct random slots."""
+    import torch
+
+    import paged_kv_cache_368_amd as pa
+
+    Hkv, B, D, NB = 40, 16, 128, 8192
+    g = torch.Generator(device="cuda").manual_seed(12)
+    kc = torch.empty((NB, Hkv, B, D), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    vc = torch.empty_like(kc).normal_(generator=g)
+    out = {}
+    for name, T in (("prompt", 8 * 2048), ("step", 64)):
+        key = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+        val = torch.empty_like(key).normal_(generator=g)
+        slots = torch.randperm(NB * B, device="cuda", generator=g)[:T].to(torch.int64)
+        for _ in range(args.warmup):
+            pa.pa_cache_write(key, val, kc, vc, slots)
+        torch.cuda.synchronize()
+        # One event pair around all the calls: a 64-token write is shorter
+        # than what a per-call event pair adds.
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            pa.pa_cache_write(key, val, kc, vc, slots)
+        b.record()
+        torch.cuda.synchronize()
+        mean = a.elapsed_time(b) / args.steps * 1e-3
+        moved = 2 * 2 * T * Hkv * D * 2 + T * 8       # rows read + written (K and V), slots read
+        out[name] = (T, mean, moved)
+    T, t, moved = out["prompt"]
+    Ts, ts, moved_s = out["step"]
+    return {
+        "metric": "KV cache write (pa_cache_write): GB/s of rows read + written into scattered slots",
+        "value": moved / t / 1e9, "unit": "GB/s (read+write)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal bf16 rows and pools, distinct random slots)",
+        "config": {"workload": "llama13b_bf16_cache_write", "num_kv_heads": Hkv, "block_size": B,
+                   "head_dim": D, "num_blocks": NB, "tokens": T},
+        "roofline": {"bound": "hbm", "achieved": moved / t / 1e9, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": moved / t / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "cache_write_kernel", "bytes_per_launch": moved,
+                     "mean_launch_us": t * 1e6},
+        "decode_step_write": {"tokens": Ts, "mean_us": ts * 1e6, "gbps": moved_s / ts / 1e9},
+        "cpu_baseline": None if args.no_cpu_baseline else _cache_write_cpu_baseline(Hkv, B, D),
+    }
+
+
+def _cache_write_cpu_baseline(Hkv, B, D) -> dict:
+    """The oracle's cache write, one token at a time, into host pools of the
+    same row shape (1024 blocks) at distinct random slots, for up to ~8 s."""
+    import numpy as np
+
+    import oracle.paged as P
+
+    NB, T = 1024, 16384
+    rng = np.random.default_rng(12)
+    kc = np.zeros((NB, Hkv, B, D), dtype=np.uint16)
+    vc = np.zeros_like(kc)
+    key = rng.integers(0, 65535, (T, Hkv, D), dtype=np.uint16)
+    val = rng.integers(0, 65535, (T, Hkv, D), dtype=np.uint16)
+    slots = rng.permutation(NB * B)[:T].astype(np.int64)
+
+    def one(i):
+        P.cache_write(kc, vc, key[i:i + 1], val[i:i + 1], slots[i:i + 1], B)
+
+    done, el = _timed_oracle(one, range(T), 8.0)
+    moved = 2 * 2 * done * Hkv * D * 2
+    return {"value": moved / el / 1e9, "unit": "GB/s (read+write)", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {T} tokens (K and V rows), numpy, 1 thread on {_cpu_name()}"}
+
+
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
 
 
@@ -412,7 +487,8 @@ def main(argv=None) -> int:
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["decode", "copy_blocks", "prefill"], default="decode",
+    ap.add_argument("--op", choices=["decode", "copy_blocks", "prefill", "cache_write"],
+                    default="decode",
                     help="decode (the headline step, default), whole-block copies, or prefill")
     ap.add_argument("--prefix", type=int, default=0,
                     help="--op prefill: tokens of each 2048-token prompt already cached")
@@ -443,6 +519,9 @@ def main(argv=None) -> int:
         return 0
     if args.op == "prefill":
         print(json.dumps(bench_prefill(args)), flush=True)
+        return 0
+    if args.op == "cache_write":
+        print(json.dumps(bench_cache_write(args)), flush=True)
         return 0
     dev_name = torch.cuda.get_device_name(0)
     print(f"[bench] device {dev_name}; building workload {args.config}", file=sys.stderr, flush=True)
