@@ -100,6 +100,34 @@ def test_cache_write_bitexact(dtype, D):
     assert from_torch(dev.value_cache, dtype).tobytes() == vc_ref.tobytes()
 
 
+@pytest.mark.parametrize("dtype,T,Hkv,D", [("bf16", 2048, 40, 128), ("f32", 4100, 8, 128),
+                                           ("f16", 2600, 64, 64)])
+def test_cache_write_prompt_sized_bitexact(dtype, T, Hkv, D):
+    """Writes of a prompt's rows (a million or more 16-byte pieces, the
+    kernel's large-write shape, with a ragged last work-group), some slots
+    negative or past the pool: the whole pools bit-exact against the
+    oracle."""
+    _say(f"cache_write prompt-sized {dtype} T={T} Hkv={Hkv} D={D}")
+    B, NB = 16, 4 * T // 16 + 7
+    rng = np.random.default_rng(25)
+    from workloads import normal_array
+    kc = normal_array(26, 52, (NB, Hkv, B, D), dtype)
+    vc = normal_array(26, 53, (NB, Hkv, B, D), dtype)
+    slots = rng.choice(NB * B, T, replace=False).astype(np.int64)
+    slots[rng.choice(T, 9, replace=False)] = -1
+    slots[rng.choice(T, 3, replace=False)] = NB * B + 5
+    key = normal_array(27, 54, (T, Hkv, D), dtype)
+    val = normal_array(27, 55, (T, Hkv, D), dtype)
+    kc_ref, vc_ref = kc.copy(), vc.copy()
+    P.cache_write(kc_ref, vc_ref, key, val, slots, B)
+    dkc, dvc = to_torch(kc, dtype, "cuda"), to_torch(vc, dtype, "cuda")
+    pa.pa_cache_write(to_torch(key, dtype, "cuda"), to_torch(val, dtype, "cuda"), dkc, dvc,
+                      torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    assert from_torch(dkc, dtype).tobytes() == kc_ref.tobytes()
+    assert from_torch(dvc, dtype).tobytes() == vc_ref.tobytes()
+
+
 def test_cache_write_llama13b_64_tokens_full_pool():
     """The 13B-shaped bf16 pool at full size, 64 new tokens at random slots:
     exactly those rows change, to exactly the written bits."""
