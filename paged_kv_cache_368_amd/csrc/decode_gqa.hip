@@ -22,13 +22,15 @@
 // remainder) so the product keeps ~16 significant bits of every weight; the
 // accumulation is fp32.
 //
-// Operand sourcing: K rows are loaded straight into the A layout (lane l:
-// token l%16, 16 bytes of dims); Q is loaded once into the B layout.  V is
-// needed with tokens along each lane (B layout of the second product), the
-// transpose of how it sits in the pool, so each chunk of V is loaded with
-// contiguous 1 KB wave loads, written to a per-wave LDS tile whose row pitch
-// is padded to D*2+8 bytes (the four token groups read by one instruction
-// fall in disjoint banks), and gathered back with 16-bit LDS reads.
+// Operand sourcing: Q is loaded once into the B layout of the first
+// product.  K and V of a chunk are loaded with contiguous 1 KB wave loads
+// (the A-operand pattern straight from memory, 16 rows x 64 B per load,
+// streams more slowly) and written to per-wave LDS tiles whose row pitch is
+// padded to D*2+32 bytes.  K is read back in the A layout (lane l: token
+// l%16, 16 bytes of dims per step); V is needed with tokens along each lane
+// (B layout of the second product), the transpose of how it sits in the
+// pool, and is read back with the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16), one per 16-dim output tile.
 //
 // Online softmax per query column, with a lazy reference: the running max m
 // is only raised when a chunk's max exceeds it by more than 8 (log2 units),
