@@ -640,25 +640,29 @@ def main(argv=None) -> int:
         sink = torch.empty(pa.PA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
         perm = torch.randperm(big.numel() * 4 // 4096, device="cuda",
                               generator=torch.Generator(device="cuda").manual_seed(0)).int()
-        # Also 4 KB tiles in random order over as many bytes as the call's K
-        # and V (a shorter read pays its ramp-up and tail on fewer bytes).
-        n_same = max(1, min(nbytes["kv"] // 4096, perm.numel()))
+        # Also the call's own pattern at its own size: its (block, kv head)
+        # tiles (B x D x element bytes) in random order over as many bytes as
+        # its K and V (a shorter read pays its ramp-up and tail on fewer
+        # bytes; fp8 tiles are half the size).
+        tile = max(1024, B * D * ELEM[wl.pool_dtype or dt])
+        n_same = max(1, min(nbytes["kv"] // tile, big.numel() * 4 // tile))
         perm_same = torch.randperm(n_same, device="cuda",
                                    generator=torch.Generator(device="cuda").manual_seed(1)).int()
         ceiling = {"how": "pa_read_probe, best of 5 HIP-event-timed calls: 2 GiB in index "
-                          "order, 2 GiB as random 4 KB tiles, the call's K+V bytes as random "
-                          "4 KB tiles"}
-        for key, buf, order in (("contiguous_gbps", big, None),
-                                ("random_4k_tiles_gbps", big, perm),
-                                ("random_4k_tiles_same_bytes_gbps", big[:n_same * 1024],
-                                 perm_same)):
-            pa.pa_read_probe(buf, 4096, order, sink)
+                          "order, 2 GiB as random 4 KB tiles, the call's K+V bytes as its own "
+                          "tiles in random order",
+                   "same_bytes_tile_bytes": tile}
+        for key, buf, tb, order in (("contiguous_gbps", big, 4096, None),
+                                    ("random_4k_tiles_gbps", big, 4096, perm),
+                                    ("random_tiles_same_bytes_gbps",
+                                     big[:n_same * tile // 4], tile, perm_same)):
+            pa.pa_read_probe(buf, tb, order, sink)
             best = float("inf")
             for _ in range(5):
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                pa.pa_read_probe(buf, 4096, order, sink)
+                pa.pa_read_probe(buf, tb, order, sink)
                 e1.record(stream)
                 torch.cuda.synchronize()
                 best = min(best, e0.elapsed_time(e1) / 1e3)
@@ -710,7 +714,7 @@ def main(argv=None) -> int:
         "read_ceiling": ceiling,
         "frac_of_tile_ceiling": (achieved / ceiling["random_4k_tiles_gbps"]) if ceiling else None,
         "frac_of_same_bytes_tile_ceiling":
-            (achieved / ceiling["random_4k_tiles_same_bytes_gbps"]) if ceiling else None,
+            (achieved / ceiling["random_tiles_same_bytes_gbps"]) if ceiling else None,
         "decode_context_tokens_per_s": sum_ctx / dec_mean_s,
         "device": dev_name,
     }
