@@ -166,9 +166,10 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
  * max_blocks_per_seq * block_size, or whose used table entries fall outside
  * [0, num_blocks), gets NaN in every output element instead of a result.
  * Supported: head_dim in {64, 128}; block_size in {16, 32, 64};
- * num_heads % num_kv_heads == 0.  fp16/bf16 with 2 <= num_heads /
- * num_kv_heads <= 16 run on the matrix cores (one work item per kv head);
- * every other case runs on the vector units (one work item per query head).
+ * num_heads % num_kv_heads == 0.  fp16/bf16 with num_heads / num_kv_heads
+ * >= 2 run on the matrix cores (one work item per kv head and tile of up to
+ * 16 of its query heads); fp32, and one query head per kv head, run on the
+ * vector units (one work item per query head).
  */
 pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const void *value_cache,
                       const int32_t *block_tables, const int32_t *context_lens,
@@ -302,7 +303,7 @@ pa_status_t pa_cache_write_fp8(const void *key, const void *value, void *key_cac
  * fp16 or bf16 (q_dtype), arithmetic is float32.  Every other argument,
  * the partition and workspace rules (size them with dtype PA_FP8_E4M3) and
  * the handling of invalid device values are those of pa_decode.  With
- * 2 <= num_heads / num_kv_heads <= 16 it runs on the matrix cores (the codes
+ * num_heads / num_kv_heads >= 2 it runs on the matrix cores (the codes
  * widened exactly to q's type), otherwise on the vector units.
  */
 pa_status_t pa_decode_fp8(void *out, const void *q, const void *key_cache,

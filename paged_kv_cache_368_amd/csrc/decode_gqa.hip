@@ -9,7 +9,11 @@
 // products.
 //
 // Work decomposition: one work-group of NW waves per (sequence, kv head,
-// partition); waves take 16-token chunks round-robin.  Per chunk:
+// tile of up to 16 query heads, partition); waves take 16-token chunks
+// round-robin.  More than 16 query heads per kv head (down to one kv head
+// for all of them) take several tiles, which the work-group order places
+// on one XCD, so after the first the kv head's K/V come from its L2.  Per
+// chunk:
 //
 //   S^T[t][q] = sum_d K[t][d] Q[q][d]      v_mfma_f32_16x16x32  (D/32 of them)
 //   O[q][d]  += sum_t P[q][t] V[t][d]      v_mfma_f32_16x16x16  (D/16 tiles)
@@ -58,7 +62,7 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyMax = 8.f;          // log2 units: weights stay <= 256
-constexpr int kGMax = 16;                // query heads per kv head on one tile
+constexpr int kGMax = kGqaTile;          // query heads per tile
 
 // Stage one 16-byte pool load (lane column col of a token row) in an LDS
 // tile row of 16-bit values: as it is, or widened from 16 E4M3 codes to 32
@@ -114,10 +118,14 @@ void decode_gqa_kernel(DecodeArgs a) {
 
   const int Hkv = a.num_kv_heads, S = a.num_seqs, H = a.num_heads;
   const int G = H / Hkv;
-  const int item = blockIdx.x;
-  const int kvh = item % Hkv;
-  const int s = (item / Hkv) % S;
-  const int p = item / (Hkv * S);
+  const int NQT = (G + kGMax - 1) / kGMax;  // query tiles per kv head
+  const int item = group_on_xcd(blockIdx.x, gridDim.x, NQT);
+  const int qt = item % NQT;
+  const int kvh = (item / NQT) % Hkv;
+  const int s = (item / (NQT * Hkv)) % S;
+  const int p = item / (NQT * Hkv * S);
+  const int Gt = min(kGMax, G - kGMax * qt);  // query heads on this tile
+  const int hb = kvh * G + kGMax * qt;        // its first query head
   const int P = a.partition_size;
   const int t0 = p * P;
   const int b0 = t0 >> a.log2_block;
@@ -132,7 +140,8 @@ void decode_gqa_kernel(DecodeArgs a) {
   // of the chunk), lane l reads row (l/LPT) + TPL*j, bytes 16*(l%LPT).
   const int v_row = lane / LPT, v_col = lane % LPT;
   const bool append = a.new_k != nullptr;                  // uniform (kernel argument)
-  // Lanes 0..LPT-1 (wave 0, row 0) write the newest token's pool rows.
+  // Lanes 0..LPT-1 (wave 0, row 0) of the first tile write the newest
+  // token's pool rows.
   const bool new_lane = append && tid < LPT;
   u32x4 nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
   if constexpr (kF8) {
@@ -161,9 +170,9 @@ void decode_gqa_kernel(DecodeArgs a) {
   }
   u32x4 qf[KI];
   {
-    const bool live = c16 < G;
+    const bool live = c16 < Gt;
     const char *qrow = reinterpret_cast<const char *>(a.q) +
-                       ((size_t)s * H + (size_t)kvh * G + (live ? c16 : 0)) * ROW;
+                       ((size_t)s * H + hb + (live ? c16 : 0)) * ROW;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const u32x4 v = *reinterpret_cast<const u32x4 *>(qrow + 64 * i + 16 * g4);
@@ -187,7 +196,7 @@ void decode_gqa_kernel(DecodeArgs a) {
   // The new token's slot, written by the partition that holds the token.
   // Like the separate cache write, it needs only the token's own slot to be
   // valid (a bad id elsewhere in the table poisons the output, not the write).
-  if (new_lane && !bad_ctx && ctx > t0 && ctx <= t1) {
+  if (new_lane && qt == 0 && !bad_ctx && ctx > t0 && ctx <= t1) {
     const int tn = ctx - 1;
     const int phys = s_tbl[(tn - t0) >> a.log2_block];
     if (phys >= 0 && phys < a.num_blocks) {
@@ -204,9 +213,9 @@ void decode_gqa_kernel(DecodeArgs a) {
 
   if (poison) {
     const float nan = __builtin_nanf("");
-    for (int idx = tid; idx < G * D; idx += NW * 64) {
+    for (int idx = tid; idx < Gt * D; idx += NW * 64) {
       const int q = idx / D, d = idx - q * D;
-      const int h = kvh * G + q;
+      const int h = hb + q;
       if (direct) {
         store_out<DT>(a.out, ((size_t)s * H + h) * D + d, &nan, 1);
       } else {
@@ -384,13 +393,13 @@ void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int q = 4 * g4 + r;
-    if (q < G) {
+    if (q < Gt) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) s_o[(wave * kGMax + q) * D + 16 * n + c16] = o[n][r];
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += NW * 64) {
+  for (int idx = tid; idx < Gt * D; idx += NW * 64) {
     const int q = idx / D, d = idx - q * D;
     float Mw = s_m[q];
 #pragma unroll
@@ -404,7 +413,7 @@ void decode_gqa_kernel(DecodeArgs a) {
       O += f * s_o[(w * kGMax + q) * D + d];
     }
     if constexpr (kF8) O *= a.v_scale;        // the tiles held V codes
-    const int h = kvh * G + q;
+    const int h = hb + q;
     if (direct) {
       const float r = L == 0.f ? 0.f : O / L;
       store_out<DT>(a.out, ((size_t)s * H + h) * D + d, &r, 1);
@@ -421,7 +430,8 @@ void decode_gqa_kernel(DecodeArgs a) {
 
 template <int DT, int KT, int D>
 hipError_t launch_gqa_t(const DecodeArgs &a, hipStream_t stream) {
-  const long n = (long)a.num_seqs * a.num_kv_heads * a.num_partitions;
+  const int G = a.num_heads / a.num_kv_heads;
+  const long n = (long)a.num_seqs * a.num_kv_heads * ((G + kGMax - 1) / kGMax) * a.num_partitions;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL((decode_gqa_kernel<DT, KT, D, kGqaWaves>), dim3((unsigned)n),
                      dim3(kGqaWaves * 64), 0, stream, a);
@@ -433,7 +443,7 @@ hipError_t launch_gqa_t(const DecodeArgs &a, hipStream_t stream) {
 bool gqa_supported(int kv_dt, int head_dim, int num_heads, int num_kv_heads) {
   const int G = num_heads / num_kv_heads;
   return (kv_dt == kF16 || kv_dt == kBF16 || kv_dt == kFP8) &&
-         (head_dim == 64 || head_dim == 128) && G >= 2 && G <= kGMax;
+         (head_dim == 64 || head_dim == 128) && G >= 2;
 }
 
 hipError_t launch_decode_gqa(const DecodeArgs &a, int dt, int kv_dt, hipStream_t stream) {

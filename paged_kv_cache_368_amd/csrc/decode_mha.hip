@@ -117,22 +117,6 @@ __device__ __forceinline__ void lane_axpy(float *o, float p, const u32x4 &v) {
   }
 }
 
-// Work-groups go to the 8 XCDs round-robin (XCD = hardware index % 8), each
-// XCD with its own L2.  Logical items run head-fastest, so the G query heads
-// that read one kv head's K/V are G consecutive items; this mapping puts
-// every such group on one XCD and next to each other in dispatch order, so
-// after the first of them the group's K/V come from that XCD's L2 (with the
-// identity mapping the G reads of a tile went to G different L2s).  Items
-// past the last whole span of 8 groups keep the identity mapping.
-__device__ __forceinline__ int group_on_xcd(int b, int n, int G) {
-  constexpr int kXcds = 8;
-  const int span = kXcds * G;
-  if (G == 1 || b >= n / span * span) return b;
-  const int blk = b / span, r = b - blk * span;
-  const int x = r % kXcds, j = r / kXcds;      // XCD x, j-th item of the span on it
-  return blk * span + x * G + j;               // head j of group blk * 8 + x
-}
-
 // DT: type of q and out; KT: storage type of the K/V pools (DT, or kFP8 with
 // DT fp16/bf16).
 template <int DT, int KT, int D, int NW>

@@ -101,7 +101,8 @@ pa_status_t plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int3
     // Work items are (sequence, query head) on the vector kernel and
     // (sequence, kv head) on the matrix-core grouped-query kernel.
     const bool gqa = pa::gqa_supported(dtype, head_dim, num_heads, num_kv_heads);
-    const long long items = (long long)num_seqs * (gqa ? num_kv_heads : num_heads);
+    const long long tiles = ceil_div(num_heads / num_kv_heads, pa::kGqaTile);
+    const long long items = (long long)num_seqs * (gqa ? num_kv_heads * tiles : num_heads);
     // The matrix-core kernel does the same per-token work over E4M3 pools
     // for half the bytes: it was measured fastest with two work-groups per CU.
     const long long min_wg = gqa && dtype == PA_FP8_E4M3 ? 2 * kMinWorkgroups : kMinWorkgroups;

@@ -67,6 +67,23 @@ __device__ __forceinline__ uint32_t fp8_pair(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 
+// Work-groups go to the 8 XCDs round-robin (XCD = hardware index % 8), each
+// XCD with its own L2.  When G consecutive logical items read the same K/V
+// (the query heads of one kv head on the vector kernel, the query tiles of
+// one kv head on the matrix-core kernel), this mapping puts every such
+// group on one XCD and next to each other in dispatch order, so after the
+// first of them the group's K/V come from that XCD's L2 (with the identity
+// mapping the G reads of a tile went to G different L2s).  Items past the
+// last whole span of 8 groups keep the identity mapping.
+__device__ __forceinline__ int group_on_xcd(int b, int n, int G) {
+  constexpr int kXcds = 8;
+  const int span = kXcds * G;
+  if (G == 1 || b >= n / span * span) return b;
+  const int blk = b / span, r = b - blk * span;
+  const int x = r % kXcds, j = r / kXcds;      // XCD x, j-th item of the span on it
+  return blk * span + x * G + j;               // head j of group blk * 8 + x
+}
+
 // Round float32 to the storage type, nearest-even; returns the storage bits.
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;

@@ -83,8 +83,9 @@ hipError_t launch_merge(const DecodeArgs &a, int dt, hipStream_t stream);
 
 // Grouped-query decode on the matrix cores: fp16/bf16 queries over pools of
 // the same type or of E4M3 codes (kv_dt), head_dim 64 or 128,
-// 2 <= num_heads / num_kv_heads <= 16.  One work item per (sequence, kv head,
-// partition) instead of per query head.
+// num_heads / num_kv_heads >= 2.  One work item per (sequence, kv head,
+// tile of up to kGqaTile query heads, partition) instead of per query head.
+constexpr int kGqaTile = 16;
 bool gqa_supported(int kv_dt, int head_dim, int num_heads, int num_kv_heads);
 hipError_t launch_decode_gqa(const DecodeArgs &a, int dt, int kv_dt, hipStream_t stream);
 

@@ -92,7 +92,7 @@ def test_append_decode_edge_contexts(dtype, B):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("H,Hkv", [(16, 2), (32, 2), (40, 40)])
+@pytest.mark.parametrize("H,Hkv", [(16, 2), (32, 2), (40, 40), (48, 1)])
 def test_append_decode_matches_step_of_three_calls(dtype, D, H, Hkv):
     """Same step through pa_compute_slots + pa_cache_write + pa_decode: the
     pools are identical and the outputs agree within the tolerance."""

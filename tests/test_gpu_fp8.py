@@ -108,6 +108,7 @@ FP8_CASES = [
     ("gqa_g16_d128", dict(ctx=[1, 16, 17, 250, 1030], H=32, Hkv=2, D=128, B=16)),
     ("gqa_g2_d64_b32", dict(ctx=[2, 31, 33, 600], H=4, Hkv=2, D=64, B=32)),
     ("gqa_g5_d128", dict(ctx=[45, 700], H=10, Hkv=2, D=128, B=16)),
+    ("mqa_g40_d128", dict(ctx=[300, 1, 77, 1100], H=40, Hkv=1, D=128, B=16)),
 ]
 
 

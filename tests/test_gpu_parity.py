@@ -298,13 +298,14 @@ def test_decode_full_size_sampled(name, idx, B):
 
 
 # ---------------------------------------------------------------------------
-# grouped-query heads: matrix-core kernel for fp16/bf16 with 2 <= G <= 16,
-# the vector kernel otherwise
+# grouped-query heads: matrix-core kernel for fp16/bf16 with G >= 2 (tiles
+# of 16 query heads), the vector kernel otherwise
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("H,Hkv", [(4, 2), (8, 2), (16, 2), (32, 2), (64, 2), (32, 32)])
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (8, 2), (16, 2), (32, 2), (64, 2), (32, 32),
+                                   (17, 1), (48, 1), (128, 2)])
 def test_decode_grouped_query(dtype, D, H, Hkv):
     _say(f"gqa {dtype} D={D} H={H}/{Hkv}")
     ctx = [1, 15, 16, 17, 100, 555, 1024, 2100]
