@@ -46,33 +46,33 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # HBM traffic of one pa_decode call, from two rocprofv3 --pmc runs of this
 # script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, summed over the
 # kernels of the call), each scaled by what the same counter reads for a
-# plain 1 GiB device copy in the same run (FETCH_SIZE reads 524,310 KiB for
-# the copy's 1,048,576 KiB of reads: factor 1.99992; WRITE_SIZE reads the
-# copy's writes exactly: factor 1.0).  An entry holds only for the kernel
+# plain 1 GiB device copy in the same run (FETCH_SIZE reads 524,300-524,320
+# KiB for the copy's 1,048,576 KiB of reads: factor ~1.9999; WRITE_SIZE
+# reads the copy's writes exactly: factor 1.0).  An entry holds only for the kernel
 # sources it was taken on (``sources`` = kernel_source_digest()); any change
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
     "llama7b_f16/B16/P4096/append": {
-        "sources": "fc88b16c18b2330fc9b33976e7dd8012cbec99c9e7f3725a6c5c74bf2fcf9ef3",
-        "fetch_kib": 328576.469, "fetch_scale": 1048576 / 524300.500,
+        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
+        "fetch_kib": 328576.391, "fetch_scale": 1048576 / 524319.250,
         "write_kib": 768.0, "write_scale": 1.0,
         "profile": "profiles/decode_mha_llama7b_f16.md"},
     # decode_gqa_kernel + merge_kernel
     "gqa70b_bf16/B16/P2048/append": {
-        "sources": "fc88b16c18b2330fc9b33976e7dd8012cbec99c9e7f3725a6c5c74bf2fcf9ef3",
-        "fetch_kib": 103365.078 + 601.500, "fetch_scale": 1048576 / 524300.500,
+        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
+        "fetch_kib": 103368.812 + 601.500, "fetch_scale": 1048576 / 524307.188,
         "write_kib": 1104.188 + 256.0, "write_scale": 1.0,
         "profile": "profiles/decode_gqa_gqa70b_bf16.md"},
     "llama7b_fp8kv/B16/P4096/append": {
-        "sources": "fc88b16c18b2330fc9b33976e7dd8012cbec99c9e7f3725a6c5c74bf2fcf9ef3",
-        "fetch_kib": 154700.328, "fetch_scale": 1048576 / 524300.500,
+        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
+        "fetch_kib": 154700.641, "fetch_scale": 1048576 / 524307.500,
         "write_kib": 512.0, "write_scale": 1.0,
         "profile": "profiles/decode_fp8_llama7b_fp8kv.md"},
     # decode_gqa_kernel over E4M3 pools + merge_kernel
     "gqa70b_fp8kv/B16/P1024/append": {
-        "sources": "fc88b16c18b2330fc9b33976e7dd8012cbec99c9e7f3725a6c5c74bf2fcf9ef3",
-        "fetch_kib": 49054.250 + 969.500, "fetch_scale": 1048576 / 524300.500,
-        "write_kib": 1824.031 + 256.0, "write_scale": 1.0,
+        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
+        "fetch_kib": 49056.250 + 969.500, "fetch_scale": 1048576 / 524307.625,
+        "write_kib": 1824.000 + 256.0, "write_scale": 1.0,
         "profile": "profiles/decode_gqa_fp8_gqa70b_fp8kv.md"},
 }
 
