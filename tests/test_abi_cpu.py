@@ -105,6 +105,21 @@ def test_partition_and_workspace_sizes(lib):
     assert pa.pa_decode_partition_size(1, 3, 2, 128, 16, 10, 0, torch.float16) == -1
 
 
+def test_automatic_partition_choices(lib):
+    """The automatic partition: one per context up to 4096 tokens (2048
+    beyond), halved while fewer than 256 work-groups would run (512 for the
+    matrix-core kernel over E4M3 pools, whose work items are (sequence, kv
+    head, tile of 16 query heads))."""
+    import torch
+    ps = pa.pa_decode_partition_size
+    assert ps(32, 32, 32, 128, 16, 2048, 0, torch.float16) == 4096     # 1024 query-head items
+    assert ps(8, 32, 32, 128, 64, 32768, 0, torch.float16) == 2048     # long contexts
+    assert ps(16, 64, 8, 128, 16, 4096, 0, torch.bfloat16) == 2048     # 128 kv-head items
+    assert lib.pa_decode_partition_size(16, 64, 8, 128, 16, 4096, 0, FP8) == 1024
+    assert ps(16, 48, 1, 128, 16, 4096, 0, torch.bfloat16) == 512      # 3 tiles of 16 heads
+    assert ps(2, 4, 4, 128, 16, 4096, 0, torch.float32) == 256         # floor of the halving
+
+
 FP8 = 3
 
 
@@ -125,7 +140,8 @@ def test_decode_fp8_rejects(lib):
     assert call(S=0, q=None, out=None) == _capi.PA_OK
     # pa_decode refuses E4M3 pools (they go through pa_decode_fp8)
     assert _decode(lib, dt=FP8) == _capi.PA_ERR_UNSUPPORTED
-    # sizing with the E4M3 pool type follows the vector kernel's work items
+    # sizing takes the E4M3 pool type (the automatic partition is pinned in
+    # test_automatic_partition_choices)
     assert lib.pa_decode_partition_size(16, 64, 8, 128, 16, 4096, 0, FP8) >= 256
     assert lib.pa_decode_workspace_size(8, 32, 32, 128, 64, 32768, 512, FP8) == \
         lib.pa_decode_workspace_size(8, 32, 32, 128, 64, 32768, 512, F16)
