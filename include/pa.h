@@ -277,8 +277,8 @@ pa_status_t pa_prefill(void *out, const void *q, const void *key_cache, const vo
 /*
  * pa_cache_write_fp8 -- pa_cache_write into E4M3 pools.  The pages advise
  * keeping the cache in a lower precision to save memory (P1 §4 keeps blocks
- * in bfloat16; P1 §5 and P2 §5 quantise and compress the cache); this build's
- * reading is 8-bit E4M3 codes with one float32 scale per pool.  Each element
+ * in bfloat16; P1 §5 and P2 §5 quantise and compress the cache); the reading
+ * taken here is 8-bit E4M3 codes with one float32 scale per pool.  Each element
  * x of a new row (storage type src_dtype, widened exactly to float32) is
  * stored as the E4M3 code nearest to x / scale (IEEE float32 division), ties
  * to the even code, magnitudes above 448 saturated to 448, NaN as 0x7F:
