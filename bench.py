@@ -68,6 +68,17 @@ COUNTERS = {
         "fetch_kib": 154700.641, "fetch_scale": 1048576 / 524307.500,
         "write_kib": 512.0, "write_scale": 1.0,
         "profile": "profiles/decode_fp8_llama7b_fp8kv.md"},
+    "llama13b_bf16/B16/P4096/append": {
+        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
+        "fetch_kib": 1311908.150, "fetch_scale": 1048576 / 524320.000,
+        "write_kib": 1920.0, "write_scale": 1.0,
+        "profile": "profiles/decode_mha_llama13b_bf16.md"},
+    # decode_mha_kernel + merge_kernel; the shared prefix is fetched once
+    "longctx_prefix_f16/B64/P512/append": {
+        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
+        "fetch_kib": 1984767.100 + 4249.050, "fetch_scale": 1048576 / 524318.600,
+        "write_kib": 9344.0 + 64.0, "write_scale": 1.0,
+        "profile": "profiles/decode_mha_longctx_prefix_f16.md"},
     # decode_gqa_kernel over E4M3 pools + merge_kernel
     "gqa70b_fp8kv/B16/P1024/append": {
         "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
