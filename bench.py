@@ -73,6 +73,16 @@ COUNTERS = {
         "fetch_kib": 1311908.150, "fetch_scale": 1048576 / 524320.000,
         "write_kib": 1920.0, "write_scale": 1.0,
         "profile": "profiles/decode_mha_llama13b_bf16.md"},
+    "llama13b_bf16/B32/P4096/append": {
+        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
+        "fetch_kib": 1311845.725, "fetch_scale": 1048576 / 524319.400,
+        "write_kib": 1920.0, "write_scale": 1.0,
+        "profile": "profiles/decode_mha_llama13b_bf16.md"},
+    "llama13b_bf16/B64/P4096/append": {
+        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
+        "fetch_kib": 1311811.725, "fetch_scale": 1048576 / 524307.200,
+        "write_kib": 1920.0, "write_scale": 1.0,
+        "profile": "profiles/decode_mha_llama13b_bf16.md"},
     # decode_mha_kernel + merge_kernel; the shared prefix is fetched once
     "longctx_prefix_f16/B64/P512/append": {
         "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
