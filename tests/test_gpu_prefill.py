@@ -155,3 +155,34 @@ def test_prefill_empty_query_ranges():
     wl, qs, q = _case("bf16", ctx, [0, 7, 0], 2, 2, 128, 16, seed=16)
     got = _run(wl, qs, q)
     BD.assert_close(got, _oracle(wl, qs, q), "bf16", "empty ranges")
+
+
+@pytest.mark.parametrize("prefix", [0, 1536])
+def test_prefill_full_size_sampled(prefix):
+    """The inputs and launch bench.py times (--op prefill): 8 LLaMA-7B-shaped
+    fp16 prompts of 2048 tokens (32 heads of 128, blocks of 16), whole or
+    the last 512 after a cached 1536-token prefix; sampled (row, head) pairs
+    against the oracle: both ends of every 256-row tile of the first and
+    last sequences, every sequence's first and last row, and random ones."""
+    S, H, D, B, n = 8, 32, 128, 16, 2048
+    L = n - prefix
+    _say(f"prefill full size, prefix {prefix}")
+    wl = build("llama7b_prefill_f16", "f16", [n] * S, H, H, D, B, seed=7, pool="permutation",
+               value_scale=0.5)
+    qs = np.arange(S + 1, dtype=np.int32) * L
+    q = normal_array(7, 40, (S * L, H, D), "f16", 0.5)
+    got = _run(wl, qs, q, max_query_len=L)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(70 + prefix)
+    rows = set()
+    for s in (0, S - 1):
+        for t0 in range(0, L, 256):
+            rows.update({(s * L + t0, int(rng.integers(H))),
+                         (s * L + min(t0 + 255, L - 1), int(rng.integers(H)))})
+    for s in range(S):
+        rows.update({(s * L, int(rng.integers(H))), (s * L + L - 1, int(rng.integers(H)))})
+    rows.update((int(rng.integers(S * L)), int(rng.integers(H))) for _ in range(48))
+    rows = sorted(rows)
+    ref = _oracle(wl, qs, q, rows)
+    idx = tuple(np.array(rows).T)
+    BD.assert_close(got[idx], ref[idx], "f16", f"prefill full size, prefix {prefix}")
