@@ -496,6 +496,119 @@ def _prefill_cpu_baseline(wl, qs, prefix) -> dict:
                       f"{prefix}-token cached prefix, float64 numpy, 1 thread on {_cpu_name()}"}
 
 
+def _bm_replay_lib(bm, events, max_blocks):
+    """Send schedule events to the library's block manager (C++ through the
+    binding); returns the number of decode-step appends."""
+    n = 0
+    for ev in events:
+        kind = ev[0]
+        if kind == "append":
+            bm.append_slots(ev[1], ev[2])
+        elif kind == "fill":
+            bm.fill_tables(ev[1], max_blocks)
+            n += len(ev[1])                      # one decode-step append per filled row
+        elif kind == "alloc":
+            bm.allocate(ev[1], ev[2])
+        elif kind == "share":
+            bm.share_prefix(ev[1], ev[2], ev[3])
+        elif kind == "free":
+            bm.free_request(ev[1])
+        elif kind == "fork":
+            bm.fork(ev[1], ev[2])
+    return n
+
+
+def _bm_replay_oracle(om, ev, max_blocks):
+    """One schedule event on the oracle's block manager (plain Python)."""
+    import numpy as np
+    kind = ev[0]
+    if kind == "append":
+        for r, p in zip(ev[1].tolist(), ev[2].tolist()):
+            om.append_slot(r, p)
+    elif kind == "fill":
+        out = np.full((len(ev[1]), max_blocks), -1, dtype=np.int32)
+        for i, r in enumerate(ev[1].tolist()):
+            t = om.table(r)
+            out[i, :len(t)] = t
+        return len(ev[1])
+    elif kind == "alloc":
+        om.allocate_for_request(ev[1], ev[2])
+    elif kind == "share":
+        om.share_prefix_blocks(ev[1], ev[2], ev[3])
+    elif kind == "free":
+        om.free_request(ev[1])
+    elif kind == "fork":
+        om.fork(ev[1], ev[2])
+    return 0
+
+
+def bench_block_manager(args) -> dict:
+    """The host block manager (include/pa_blocks.h, C++) on a continuous-
+    batching decode schedule: 256 live requests, prompts of 512-2048 tokens
+    (a quarter start from a shared 1024-token system prompt), 32-256
+    generated tokens each, then freed and replaced, occasional beam forks
+    (copy on write at the next append); blocks of 16 tokens.  Each decode
+    step is one pa_bm_append_slots over the batch and one pa_bm_fill_tables
+    (pa_decode's block_tables), through the Python binding as a serving loop
+    would call it.  Host only: no GPU is used."""
+    import workloads as W
+    from paged_kv_cache_368_amd.blocks import BlockManager
+
+    batch, B, NB = 256, 16, 48000
+    max_blocks = (2048 + 256) // B + 1
+    steps = max(args.steps, 1) * 10
+    warm = max(args.warmup, 0) * 10
+    setup, per_step = W.block_manager_schedule(5, batch, warm + steps)
+    bm = BlockManager(NB, B)
+    _bm_replay_lib(bm, setup, max_blocks)
+    for ev in per_step[:warm]:
+        _bm_replay_lib(bm, ev, max_blocks)
+    t0 = time.perf_counter()
+    appends = 0
+    for ev in per_step[warm:]:
+        appends += _bm_replay_lib(bm, ev, max_blocks)
+    el = time.perf_counter() - t0
+    free, used, nreq = bm.stats()
+    bm.close()
+    out = {
+        "metric": "host block manager: decode-step token appends/s (append_slots + fill_tables "
+                  "per step, continuous batching)",
+        "value": appends / el, "unit": "appended tokens/s", "n_gpus": 0, "steps": steps,
+        "warmup": warm, "ms_per_step": el * 1e3 / steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic seeded request schedule (workloads.block_manager_schedule)",
+        "config": {"workload": "block_manager_continuous_batching", "live_requests": batch,
+                   "block_size": B, "num_blocks": NB, "prompt_tokens": [512, 2048],
+                   "generated_tokens": [32, 256], "shared_system_prompt": 1024,
+                   "blocks_in_use_at_end": used, "requests_at_end": nreq},
+        "roofline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else _bm_cpu_baseline(setup, per_step,
+                                                                           NB, B, max_blocks),
+    }
+    return out
+
+
+def _bm_cpu_baseline(setup, per_step, NB, B, max_blocks) -> dict:
+    """The oracle's block manager (plain Python) on the same schedule from its
+    start, until ~10 s are spent."""
+    import oracle.blocks as OB
+    om = OB.BlockManager(NB, B)
+    for ev in setup:
+        _bm_replay_oracle(om, ev, max_blocks)
+    appends, steps_done = 0, 0
+    t0 = time.perf_counter()
+    for st in per_step:
+        for ev in st:
+            appends += _bm_replay_oracle(om, ev, max_blocks)
+        steps_done += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    el = time.perf_counter() - t0
+    return {"value": appends / el, "unit": "appended tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {steps_done} decode steps of the same schedule (after its "
+                      f"setup), plain Python, 1 thread on {_cpu_name()}"}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -508,9 +621,11 @@ def main(argv=None) -> int:
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["decode", "copy_blocks", "prefill", "cache_write"],
+    ap.add_argument("--op", choices=["decode", "copy_blocks", "prefill", "cache_write",
+                                     "block_manager"],
                     default="decode",
-                    help="decode (the headline step, default), whole-block copies, or prefill")
+                    help="decode (the headline step, default), whole-block copies, prefill, "
+                         "the cache write, or the host block manager")
     ap.add_argument("--prefix", type=int, default=0,
                     help="--op prefill: tokens of each 2048-token prompt already cached")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs for --op copy_blocks")
@@ -527,6 +642,10 @@ def main(argv=None) -> int:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
+
+    if args.op == "block_manager":                   # host only
+        print(json.dumps(bench_block_manager(args)), flush=True)
+        return 0
 
     import torch
 

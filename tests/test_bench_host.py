@@ -28,3 +28,18 @@ def test_total_bytes_tiny_workload():
 def test_multi_gpu_request_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_block_manager_op_runs_on_the_host():
+    """bench.py --op block_manager needs no GPU and prints the contract's
+    fields for its host-side line."""
+    import argparse
+
+    import paged_kv_cache_368_amd as pa
+    if not os.path.exists(pa.LIB_PATH):
+        from paged_kv_cache_368_amd.build import build
+        build()
+    r = bench.bench_block_manager(argparse.Namespace(steps=2, warmup=1, no_cpu_baseline=True))
+    assert r["value"] > 0 and r["unit"] == "appended tokens/s" and r["steps"] == 20
+    assert r["config"]["workload"] == "block_manager_continuous_batching"
+    assert r["roofline"] is None and r["cpu_baseline"] is None

@@ -201,3 +201,51 @@ def test_argument_errors():
         bm.allocate(1, -1)
     assert e.value.status == _capi.PA_ERR_INVALID_ARGUMENT
     assert "num_tokens" in pa.pa_last_error()
+
+
+def test_continuous_batching_schedule_matches_oracle():
+    """The request schedule bench.py --op block_manager replays (scaled
+    down): prompts, a shared system prompt, per-step batched appends, table
+    export, frees and beam forks with copy on write.  Every slot, every
+    copy-on-write pair, every exported table and the final state agree."""
+    import workloads as W
+    B, NB, MB = 16, 4000, 20
+    setup, per_step = W.block_manager_schedule(3, 24, 60, system_prompt=64,
+                                               prompt=(20, 200), generate=(3, 40),
+                                               fork_prob=0.3)
+    assert any(e[0] == "fork" for st in per_step for e in st)
+    assert any(e[0] == "share" for e in setup) or any(e[0] == "share" for st in per_step for e in st)
+    cpp, ref = BlockManager(NB, B), OB.BlockManager(NB, B)
+    copies = 0
+    for ev in setup + [e for st in per_step for e in st]:
+        kind = ev[0]
+        if kind == "append":
+            slots, pairs = cpp.append_slots(ev[1], ev[2])
+            want_slots, want_pairs = [], []
+            for r, p in zip(ev[1].tolist(), ev[2].tolist()):
+                slot, _, cp = ref.append_slot(r, p)
+                want_slots.append(slot)
+                if cp is not None:
+                    want_pairs.append(list(cp))
+            assert slots.tolist() == want_slots
+            assert pairs.tolist() == want_pairs
+            copies += len(want_pairs)
+        elif kind == "fill":
+            got = cpp.fill_tables(ev[1], MB)
+            for i, r in enumerate(ev[1].tolist()):
+                t = ref.table(r)
+                assert got[i, :len(t)].tolist() == t and (got[i, len(t):] == -1).all()
+        elif kind == "alloc":
+            assert cpp.allocate(ev[1], ev[2]) == ref.allocate_for_request(ev[1], ev[2])
+        elif kind == "share":
+            cpp.share_prefix(ev[1], ev[2], ev[3])
+            ref.share_prefix_blocks(ev[1], ev[2], ev[3])
+        elif kind == "free":
+            cpp.free_request(ev[1])
+            ref.free_request(ev[1])
+        elif kind == "fork":
+            cpp.fork(ev[1], ev[2])
+            ref.fork(ev[1], ev[2])
+    assert copies > 0
+    _same_state(cpp, ref)
+    cpp.close()

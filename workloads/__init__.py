@@ -406,3 +406,80 @@ def to_device(wl: Workload, device="cuda") -> DeviceWorkload:
         new_value=to_torch(wl.new_value, wl.dtype, device),
         out=torch.empty_like(q),
     )
+
+
+# ---------------------------------------------------------------------------
+# Block-manager schedules (host side): the request events a continuous-
+# batching decode loop sends to a block manager.  Pure bookkeeping of request
+# lengths; nothing here depends on which blocks a manager hands out.
+# ---------------------------------------------------------------------------
+
+SYSTEM_PROMPT_ID = 1 << 40
+
+
+def block_manager_schedule(seed: int, batch: int, steps: int, system_prompt: int = 1024,
+                           share_frac: float = 0.25, fork_prob: float = 0.02,
+                           prompt=(512, 2048), generate=(32, 256)):
+    """Events of ``steps`` decode steps over ``batch`` live requests.
+
+    Returns ``(setup, per_step)``: ``setup`` admits the system prompt and the
+    first ``batch`` requests; ``per_step[k]`` is the events of step k.  Events:
+      ("alloc", rid, num_tokens)          prompt allocation
+      ("share", src, dst, shared_len)     prefix sharing of the system prompt
+      ("append", rids, positions)         int64 / int32 arrays, in order
+      ("fill", rids)                      the step's block tables for decode
+      ("free", rid)                       a finished request
+      ("fork", src, dst)                  a beam fork of a live request
+    A request's prompt length is uniform in ``prompt``; ``share_frac`` of the
+    requests start from the system prompt (shared, then their own tokens
+    appended one position at a time); each generates a number of tokens
+    uniform in ``generate`` and is then freed and replaced.  Each step every
+    live request appends the token at its current length."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(98,))))
+    live: dict[int, list[int]] = {}
+    next_id = [0]
+
+    def admit(ev):
+        rid = next_id[0]
+        next_id[0] += 1
+        plen = int(rng.integers(prompt[0], prompt[1] + 1))
+        if rng.random() < share_frac:
+            plen = max(plen, system_prompt)
+            ev.append(("share", SYSTEM_PROMPT_ID, rid, system_prompt))
+            if plen > system_prompt:
+                ev.append(("append", np.full(plen - system_prompt, rid, dtype=np.int64),
+                           np.arange(system_prompt, plen, dtype=np.int32)))
+        else:
+            ev.append(("alloc", rid, plen))
+        live[rid] = [plen, int(rng.integers(generate[0], generate[1] + 1))]
+
+    setup = [("alloc", SYSTEM_PROMPT_ID, system_prompt)]
+    for _ in range(batch):
+        admit(setup)
+    per_step = []
+    for _ in range(steps):
+        ev = []
+        rids = np.fromiter(live.keys(), dtype=np.int64, count=len(live))
+        pos = np.array([live[int(r)][0] for r in rids], dtype=np.int32)
+        ev.append(("append", rids, pos))
+        ev.append(("fill", rids))
+        done = []
+        for r in rids:
+            st = live[int(r)]
+            st[0] += 1
+            st[1] -= 1
+            if st[1] <= 0:
+                done.append(int(r))
+        for r in done:
+            ev.append(("free", r))
+            del live[r]
+            admit(ev)
+        if rng.random() < fork_prob * len(live) / max(batch, 1):
+            src = int(rids[int(rng.integers(len(rids)))])
+            if src in live:
+                dst = next_id[0]
+                next_id[0] += 1
+                ev.append(("fork", src, dst))
+                live[dst] = [live[src][0], int(rng.integers(generate[0], generate[1] + 1))]
+        per_step.append(ev)
+    return setup, per_step
