@@ -351,18 +351,23 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
   if (wrows == 0) return;
 
   // out = O / l for each row this lane holds (rows 4*g4 + r of subtile u,
-  // dims 16n + c16).
+  // dims 16n + c16), as O times one reciprocal per row (v_rcp_f32, within
+  // an ulp): a row with context has l >= 1, since its reference max is one
+  // of its own scores, whose weight is at least 1; an empty row has l = 0
+  // and gives 0.  (IEEE division of every element cost the work-group's
+  // tail ~950 VALU instructions per wave.)
 #pragma unroll
   for (int u = 0; u < kSub; ++u) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int q = 4 * g4 + r;
       const float lr = lsum[u][r];
+      const float inv = lr == 0.f ? 0.f : __builtin_amdgcn_rcpf(lr);
       if (q < srows[u]) {
         const size_t rowbase = ((size_t)(q0 + r0 + wr0 + 16 * u + q) * H + h) * D;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const float v = lr == 0.f ? 0.f : o[u][n][r] / lr;
+          const float v = o[u][n][r] * inv;
           store_out<DT>(a.out, rowbase + 16 * n + c16, &v, 1);
         }
       }
