@@ -1,0 +1,61 @@
+"""The C ABI used without PyTorch: paged_kv_cache_368_amd/pa_decode_step
+(examples/decode_step.cpp, built beside libpa.so) runs one decode step
+through pa_compute_slots, pa_cache_write and pa_decode on device memory it
+allocates itself with the HIP runtime.  Its slots and pools must equal the
+oracle's bit for bit and its outputs must be within the decode tolerance."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.paged as P
+import tests._bounds as BD
+import paged_kv_cache_368_amd as pa
+from paged_kv_cache_368_amd.build import EXAMPLE
+from workloads import build
+
+pytestmark = pytest.mark.gpu
+
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert os.path.exists(EXAMPLE), f"{EXAMPLE} is missing: run the package build"
+
+
+@pytest.mark.parametrize("dtype,H,Hkv,D,B,ps", [("bf16", 8, 2, 128, 16, 256),
+                                                ("f16", 4, 4, 128, 32, 0),
+                                                ("f32", 4, 4, 64, 16, 64)])
+def test_decode_step_through_the_c_abi(tmp_path, dtype, H, Hkv, D, B, ps):
+    print(f"[case] C-ABI decode step {dtype} H={H}/{Hkv} D={D} B={B} P={ps}", flush=True)
+    sys.stdout.flush()
+    wl = build("cabi", dtype, [1, 17, 300, 1000, 33], H, Hkv, D, B, seed=95 + D + B,
+               pool="choice", pool_factor=1.3)
+    S, NB, MB = wl.num_seqs, wl.num_blocks, wl.block_tables.shape[1]
+    with open(tmp_path / "meta.txt", "w") as f:
+        f.write(f"{S} {H} {Hkv} {D} {B} {NB} {MB} {DTYPE_CODE[dtype]} {wl.max_context_len} "
+                f"{wl.scale!r} {ps}\n")
+    for name, arr in (("q", wl.q), ("kc", wl.key_cache), ("vc", wl.value_cache),
+                      ("tables", wl.block_tables.astype(np.int32)),
+                      ("ctx", wl.context_lens.astype(np.int32)), ("new_k", wl.new_key),
+                      ("new_v", wl.new_value)):
+        np.ascontiguousarray(arr).tofile(tmp_path / f"{name}.bin")
+    r = subprocess.run([EXAMPLE, str(tmp_path)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+    slots = np.fromfile(tmp_path / "slots.bin", dtype=np.int64)
+    want = P.compute_slots(wl.block_tables, B, NB, context_lens=wl.context_lens)
+    assert np.array_equal(slots, want)
+    kc, vc = wl.key_cache.copy(), wl.value_cache.copy()
+    P.cache_write(kc, vc, wl.new_key, wl.new_value, want, B)
+    assert np.fromfile(tmp_path / "kc_out.bin", dtype=kc.dtype).tobytes() == kc.tobytes()
+    assert np.fromfile(tmp_path / "vc_out.bin", dtype=vc.dtype).tobytes() == vc.tobytes()
+    got = np.fromfile(tmp_path / "out.bin", dtype=wl.q.dtype).reshape(wl.q.shape)
+    ref = P.paged_decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, B, wl.scale, dtype, Hkv)
+    BD.assert_close(P.to_f64(got, dtype), ref, dtype, "C-ABI decode step")
