@@ -21,7 +21,6 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
-EXAMPLE = os.path.join(PKG, "pa_decode_step")       # examples/decode_step.cpp, built beside it
 
 SOURCES = ["pa_abi.cpp", "block_manager.cpp", "decode_mha.hip", "decode_gqa.hip", "cache_write.hip", "block_copy.hip", "prefill.hip", "read_probe.hip"]
 ARCH = "gfx950"
@@ -57,22 +56,9 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
-    _build_example()
     if verbose:
-        print(f"built {LIB} and {EXAMPLE}")
+        print(f"built {LIB}")
     return LIB
-
-
-def _build_example() -> None:
-    """The C-ABI example (examples/decode_step.cpp): host code only, linked
-    against libpa.so beside it."""
-    src = os.path.join(PKG, "examples", "decode_step.cpp")
-    cmd = [HIPCC, "-O2", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-x", "hip", src,
-           "-L", PKG, "-lpa", "-Wl,-rpath,$ORIGIN", "-o", EXAMPLE + ".tmp"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for the example:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(EXAMPLE + ".tmp", EXAMPLE)
 
 
 if __name__ == "__main__":
