@@ -429,26 +429,33 @@ def bench_prefill(args) -> dict:
 
     S, H, D, B, n = 8, 32, 128, 16, 2048
     L = n - args.prefix
+    fp8 = getattr(args, "kv", "f16") == "fp8"
     wl = build("llama7b_prefill_f16", "f16", [n] * S, H, H, D, B, seed=7, pool="permutation",
-               value_scale=0.5)
+               value_scale=0.5, kv_dtype="fp8" if fp8 else None, kv_scale=0.5)
     qs = np.arange(S + 1, dtype=np.int32) * L
     q = to_torch(normal_array(7, 40, (S * L, H, D), "f16", 0.5), "f16", "cuda")
-    kc, vc = to_torch(wl.key_cache, "f16", "cuda"), to_torch(wl.value_cache, "f16", "cuda")
+    kc, vc = to_torch(wl.key_cache, wl.pool_dtype, "cuda"), to_torch(wl.value_cache, wl.pool_dtype, "cuda")
     bt = torch.tensor(wl.block_tables, device="cuda")
     cl = torch.tensor(wl.context_lens, device="cuda")
     qst = torch.tensor(qs, device="cuda")
     out = torch.empty_like(q)
     flops = prefill_flops(wl.context_lens, [L] * S, H, D)
+
+    def call():
+        if fp8:
+            pa.pa_prefill_fp8(out, q, kc, vc, bt, cl, qst, L, n, wl.k_scale, wl.v_scale, wl.scale)
+        else:
+            pa.pa_prefill(out, q, kc, vc, bt, cl, qst, L, n, wl.scale)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
-        pa.pa_prefill(out, q, kc, vc, bt, cl, qst, L, n, wl.scale)
+        call()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in ev:
         a.record()
-        pa.pa_prefill(out, q, kc, vc, bt, cl, qst, L, n, wl.scale)
+        call()
         b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -462,7 +469,7 @@ def bench_prefill(args) -> dict:
         "data": "synthetic (seeded N(0,1)*0.5 q/K/V, random block tables)",
         "config": {"workload": "llama7b_prefill_f16", "num_seqs": S, "num_heads": H,
                    "head_dim": D, "block_size": B, "context_len": n, "query_len": L,
-                   "cached_prefix": args.prefix},
+                   "cached_prefix": args.prefix, "kv": "fp8 E4M3" if fp8 else "f16"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS["f16"],
                      "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"], "traffic": None,
                      "kernel": "prefill_kernel", "flops_per_launch": flops,
@@ -486,8 +493,13 @@ def _prefill_cpu_baseline(wl, qs, prefix) -> dict:
     items = [items[k] for k in order]
 
     def one(item):
-        P.paged_prefill(q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens, qs,
-                        wl.block_size, wl.scale, wl.dtype, wl.num_kv_heads, rows=[item])
+        if wl.pool_dtype == "fp8":
+            P.paged_prefill_fp8(q, wl.key_cache, wl.value_cache, wl.block_tables,
+                                wl.context_lens, qs, wl.block_size, wl.scale, wl.dtype,
+                                wl.k_scale, wl.v_scale, wl.num_kv_heads, rows=[item])
+        else:
+            P.paged_prefill(q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens,
+                            qs, wl.block_size, wl.scale, wl.dtype, wl.num_kv_heads, rows=[item])
 
     done, el = _timed_oracle(one, items, 12.0)
     return {"value": done / wl.num_heads / el, "unit": "query tokens/s", "cores": 1,
@@ -626,6 +638,8 @@ def main(argv=None) -> int:
                     default="decode",
                     help="decode (the headline step, default), whole-block copies, prefill, "
                          "the cache write, or the host block manager")
+    ap.add_argument("--kv", choices=["f16", "fp8"], default="f16",
+                    help="--op prefill: K/V pools in fp16 or as E4M3 codes (pa_prefill_fp8)")
     ap.add_argument("--prefix", type=int, default=0,
                     help="--op prefill: tokens of each 2048-token prompt already cached")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs for --op copy_blocks")

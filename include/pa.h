@@ -275,6 +275,32 @@ pa_status_t pa_prefill(void *out, const void *q, const void *key_cache, const vo
                        pa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * pa_prefill_fp8 -- pa_prefill over E4M3 pools (the lower-precision cache of
+ * P1 §4-§5 and P2 §5, in the reading pa_cache_write_fp8 documents): a
+ * prompt's query rows attend causally to a context whose K/V are stored as
+ * codes, value = decode(code) * k_scale (K) or * v_scale (V), e.g. a cached
+ * prefix written by pa_cache_write_fp8 (P3 §3).  Row j of sequence s at
+ * position p = context_lens[s] - qlen + j gets
+ *   out = softmax(scale * q . k_t, t = 0..p) . v_t
+ * over those values, computed in float32.
+ *   key_cache, value_cache  in  uint8 E4M3 codes [num_blocks][num_kv_heads][block_size][head_dim]
+ *   k_scale, v_scale        in  the pools' scales (finite, > 0)
+ *   dtype                   q's and out's type: PA_F16 or PA_BF16
+ *   every other argument as for pa_prefill.
+ * Errors as for pa_prefill; PA_ERR_INVALID_ARGUMENT for a scale that is not
+ * finite and positive.  Device-resident values poison only their rows, as
+ * for pa_prefill.
+ */
+pa_status_t pa_prefill_fp8(void *out, const void *q, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, const int32_t *query_start,
+                           int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                           int32_t max_context_len, float scale, float k_scale, float v_scale,
+                           pa_dtype_t dtype, hipStream_t stream);
+
+/*
  * pa_cache_write_fp8 -- pa_cache_write into E4M3 pools.  The pages advise
  * keeping the cache in a lower precision to save memory (P1 §4 keeps blocks
  * in bfloat16; P1 §5 and P2 §5 quantise and compress the cache); the reading

@@ -393,6 +393,32 @@ def paged_decode_fp8(q, key_cache, value_cache, block_tables, context_lens, bloc
     return out
 
 
+def paged_prefill_fp8(q, key_cache, value_cache, block_tables, context_lens, query_start,
+                      block_size: int, scale: float, q_dtype: str, k_scale: float,
+                      v_scale: float, num_kv_heads: int | None = None, rows=None) -> np.ndarray:
+    """``paged_prefill`` over E4M3 pools: query row j of sequence s (position
+    p = ctx - qlen + j) gathers the codes of tokens 0..p through the table,
+    takes their values decode(code) * pool scale in float64, and attends."""
+    q64 = to_f64(q, q_dtype)
+    T, H, D = q64.shape
+    Hkv = key_cache.shape[1] if num_kv_heads is None else num_kv_heads
+    ks, vs = float(np.float32(k_scale)), float(np.float32(v_scale))
+    seq_of = np.full(T, -1, dtype=np.int64)
+    for s in range(len(context_lens)):
+        seq_of[int(query_start[s]):int(query_start[s + 1])] = s
+    out = np.full((T, H, D), np.nan)
+    todo = rows if rows is not None else [(i, h) for i in range(T) for h in range(H)]
+    for i, h in todo:
+        s = int(seq_of[i])
+        qlen = int(query_start[s + 1]) - int(query_start[s])
+        n = int(context_lens[s]) - qlen + (i - int(query_start[s])) + 1
+        g = kv_head_of(h, H, Hkv)
+        K = e4m3_decode(gather_context(key_cache, block_tables[s], n, g, block_size)) * ks
+        V = e4m3_decode(gather_context(value_cache, block_tables[s], n, g, block_size)) * vs
+        out[i, h] = attention(q64[i, h], K, V, scale)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Byte accounting -- P2 §2.2: KV bytes = 2 x tokens x layers x heads x
 # head_dim x element bytes.

@@ -24,6 +24,7 @@ from ._capi import (  # noqa: F401
     pa_decode_workspace_size,
     pa_last_error,
     pa_prefill,
+    pa_prefill_fp8,
     pa_read_probe,
     pa_version,
 )

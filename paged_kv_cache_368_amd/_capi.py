@@ -74,6 +74,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_prefill.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, i32,
                                i32, i32, i32, i32, f32, c.c_int, ptr]
     lib.pa_prefill.restype = st
+    lib.pa_prefill_fp8.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32,
+                                   i32, i32, i32, i32, i32, f32, f32, f32, c.c_int, ptr]
+    lib.pa_prefill_fp8.restype = st
     lib.pa_copy_blocks.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, c.c_int64, i32, i32, ptr]
     lib.pa_copy_blocks.restype = st
     lib.pa_last_error.argtypes = []
@@ -332,6 +335,45 @@ def pa_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
         ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(context_lens.data_ptr()),
         ctypes.c_void_p(query_start.data_ptr()), S, T, H, Hkv, D, B, NB, block_tables.shape[1],
         max_query_len, max_context_len, float(scale), DTYPE_CODES[q.dtype], _stream(q)))
+    return out
+
+
+def pa_prefill_fp8(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                   value_cache: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, query_start: torch.Tensor, max_query_len: int,
+                   max_context_len: int, k_scale: float, v_scale: float,
+                   scale: float | None = None) -> torch.Tensor:
+    """pa_prefill over uint8 E4M3 pools (values code * scale): query rows
+    ``q`` [T][H][D] (fp16/bf16) into ``out``; see include/pa.h."""
+    lib = load_library()
+    for n, t in (("out", out), ("q", q), ("key_cache", key_cache), ("value_cache", value_cache),
+                 ("block_tables", block_tables), ("context_lens", context_lens),
+                 ("query_start", query_start)):
+        _dev(t, n)
+    if q.dtype not in (torch.float16, torch.bfloat16) or out.dtype != q.dtype:
+        raise ValueError("q and out must share float16 or bfloat16")
+    if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8:
+        raise ValueError("E4M3 pools are uint8 tensors")
+    for n, t in (("block_tables", block_tables), ("context_lens", context_lens),
+                 ("query_start", query_start)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{n} must be int32")
+    T, H, D = q.shape
+    NB, Hkv, B, D2 = key_cache.shape
+    S = context_lens.numel()
+    if D2 != D or tuple(value_cache.shape) != (NB, Hkv, B, D) or tuple(out.shape) != (T, H, D):
+        raise ValueError("shape mismatch between q, out and the pools")
+    if block_tables.shape[0] != S or query_start.numel() != S + 1:
+        raise ValueError("block_tables needs one row and query_start S + 1 entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(lib.pa_prefill_fp8(
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(context_lens.data_ptr()),
+        ctypes.c_void_p(query_start.data_ptr()), S, T, H, Hkv, D, B, NB, block_tables.shape[1],
+        max_query_len, max_context_len, float(scale), float(k_scale), float(v_scale),
+        DTYPE_CODES[q.dtype], _stream(q)))
     return out
 
 

@@ -396,18 +396,29 @@ pa_status_t pa_decode_fp8(void *out, const void *q, const void *key_cache,
                      partition_size, workspace, workspace_bytes, q_dtype, PA_FP8_E4M3, stream);
 }
 
-pa_status_t pa_prefill(void *out, const void *q, const void *key_cache, const void *value_cache,
-                       const int32_t *block_tables, const int32_t *context_lens,
-                       const int32_t *query_start, int32_t num_seqs, int32_t num_tokens,
-                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                       int32_t max_query_len, int32_t max_context_len, float scale,
-                       pa_dtype_t dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_prefill and pa_prefill_fp8: q/out of type dtype, pools of type kv_dt
+// (dtype, or PA_FP8_E4M3 with its two pool scales).
+pa_status_t prefill_impl(void *out, const void *q, const void *key_cache, const void *value_cache,
+                         const int32_t *block_tables, const int32_t *context_lens,
+                         const int32_t *query_start, int32_t num_seqs, int32_t num_tokens,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_query_len, int32_t max_context_len, float scale,
+                         float k_scale, float v_scale, pa_dtype_t dtype, pa_dtype_t kv_dt,
+                         hipStream_t stream) {
   pa_status_t st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                max_context_len, dtype);
   if (st != PA_OK) return st;
   if (dtype != PA_F16 && dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "pa_prefill takes fp16 or bf16");
+    return fail(PA_ERR_UNSUPPORTED, kv_dt == PA_FP8_E4M3 ? "pa_prefill_fp8 takes fp16 or bf16 queries"
+                                                          : "pa_prefill takes fp16 or bf16");
+  if (kv_dt == PA_FP8_E4M3 && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) &&
+                                v_scale > 0.f))
+    return fail(PA_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be finite and > 0");
   if (num_tokens < 0 || max_query_len < 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens and max_query_len must be >= 0");
   if (max_query_len > max_context_len)
@@ -446,10 +457,42 @@ pa_status_t pa_prefill(void *out, const void *q, const void *key_cache, const vo
   a.max_query_len = max_query_len;
   a.max_context_len = max_context_len;
   a.num_tiles = (int)tiles;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = pa::launch_prefill(a, dtype, stream);
+  a.scale_log2 = scale * (kv_dt == PA_FP8_E4M3 ? k_scale : 1.f) * 1.4426950408889634f;
+  a.v_scale = kv_dt == PA_FP8_E4M3 ? v_scale : 1.f;
+  hipError_t e = pa::launch_prefill(a, dtype, kv_dt, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_prefill(void *out, const void *q, const void *key_cache, const void *value_cache,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       const int32_t *query_start, int32_t num_seqs, int32_t num_tokens,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_query_len, int32_t max_context_len, float scale,
+                       pa_dtype_t dtype, hipStream_t stream) {
+  return prefill_impl(out, q, key_cache, value_cache, block_tables, context_lens, query_start,
+                      num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                      num_blocks, max_blocks_per_seq, max_query_len, max_context_len, scale, 1.f,
+                      1.f, dtype, dtype, stream);
+}
+
+pa_status_t pa_prefill_fp8(void *out, const void *q, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, const int32_t *query_start,
+                           int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                           int32_t max_context_len, float scale, float k_scale, float v_scale,
+                           pa_dtype_t dtype, hipStream_t stream) {
+  return prefill_impl(out, q, key_cache, value_cache, block_tables, context_lens, query_start,
+                      num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                      num_blocks, max_blocks_per_seq, max_query_len, max_context_len, scale,
+                      k_scale, v_scale, dtype, PA_FP8_E4M3, stream);
 }
 
 pa_status_t pa_cache_write_fp8(const void *key, const void *value, void *key_cache,

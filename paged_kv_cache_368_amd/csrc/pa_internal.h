@@ -71,12 +71,13 @@ struct PrefillArgs {
   int block_size, log2_block, num_blocks, max_blocks_per_seq;
   int max_query_len, max_context_len;
   int num_tiles;             // ceil(max_query_len / rows per tile)
-  float scale_log2;
+  float scale_log2;          // score scale (times the K scale over E4M3 pools) x log2(e)
+  float v_scale;             // E4M3 pools: the V scale, applied to the outputs
 };
 
 // Paged prefill on the matrix cores: fp16/bf16, head_dim 64 or 128.
 int prefill_rows_per_tile();
-hipError_t launch_prefill(const PrefillArgs &a, int dt, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, int dt, int kv_dt, hipStream_t stream);
 
 hipError_t launch_decode_mha(const DecodeArgs &a, int dt, int kv_dt, hipStream_t stream);
 hipError_t launch_merge(const DecodeArgs &a, int dt, hipStream_t stream);

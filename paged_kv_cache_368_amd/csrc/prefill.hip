@@ -73,9 +73,14 @@ __device__ __forceinline__ uint32_t pack_lo_bf16(float a, float b) {
                                0x07060302u);
 }
 
-template <int DT, int D>
+// KT: the pools' storage type, DT or kFP8 (E4M3 codes, widened exactly to
+// DT as they are staged in LDS, so the tiles and products are DT's).
+template <int DT, int KT, int D>
 __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(KT == DT || KT == kFP8, "pool type");
+  constexpr bool kF8 = KT == kFP8;
+  constexpr int EKV = kF8 ? 1 : 2;           // bytes per element of the pools
   static_assert(kPfWaves * 64 >= kMaxPartBlocks, "one thread per staged block id");
   constexpr int E = 2;
   constexpr int ROW = D * E;                 // bytes per token row
@@ -158,8 +163,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
 
   const size_t head_stride = (size_t)a.block_size * D;
   const size_t block_stride = head_stride * a.num_kv_heads;
-  const char *kbase = reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E;
-  const char *vbase = reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E;
+  const char *kbase = reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * EKV;
+  const char *vbase = reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * EKV;
 
   // DMA addressing: lane l of a 1 KB load lands at LDS byte 16l of it, i.e.
   // row l / PIECES, physical piece l % PIECES, which holds logical piece
@@ -327,6 +332,56 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
       }
     };
 
+    if constexpr (kF8) {
+      // E4M3 pools: thread t < 2D loads 16 codes of one row of the chunk
+      // (row t / (D/16), bytes 16 (t % (D/16)) ..) into registers one chunk
+      // ahead, and widens them into the swizzled tile once the stage is free.
+      constexpr int TPR = D / 16;                      // threads per pool row
+      const bool stager = tid < kCh * TPR;
+      const int srow = tid / TPR, spart = tid % TPR;
+      u32x4 ck = {0u, 0u, 0u, 0u}, cv = {0u, 0u, 0u, 0u};
+      auto fload = [&](int k) __attribute__((always_inline)) {
+        ck = u32x4{0u, 0u, 0u, 0u};
+        cv = u32x4{0u, 0u, 0u, 0u};
+        const int t = w0 + k * kCh + srow;
+        if (stager && t < wend) {                      // rows past the window stay zero
+          const int phys = s_tbl[(t - w0) >> a.log2_block];
+          const size_t off = ((size_t)phys * block_stride + (size_t)(t & (a.block_size - 1)) * D) +
+                             16 * spart;
+          ck = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kbase + off));
+          cv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vbase + off));
+        }
+      };
+      auto put = [&](unsigned char *st, const u32x4 &w) __attribute__((always_inline)) {
+        const u32x4 lo = {fp8_pair<DT, false>(w.x), fp8_pair<DT, true>(w.x),
+                          fp8_pair<DT, false>(w.y), fp8_pair<DT, true>(w.y)};
+        const u32x4 hi = {fp8_pair<DT, false>(w.z), fp8_pair<DT, true>(w.z),
+                          fp8_pair<DT, false>(w.w), fp8_pair<DT, true>(w.w)};
+        const int sw = srow % PIECES;
+        *reinterpret_cast<u32x4 *>(st + srow * ROW + (((2 * spart) ^ sw) << 4)) = lo;
+        *reinterpret_cast<u32x4 *>(st + srow * ROW + (((2 * spart + 1) ^ sw) << 4)) = hi;
+      };
+      auto fcommit = [&](unsigned char *sk, unsigned char *sv) __attribute__((always_inline)) {
+        if (stager) {
+          put(sk, ck);
+          put(sv, cv);
+        }
+      };
+      fload(0);
+      fcommit(s_k0, s_v0);
+      for (int k = 0; k < nch; k += 2) {
+        __syncthreads();                               // chunk k in stage 0; stage 1 is free
+        if (k + 1 < nch) fload(k + 1);
+        compute(k, s_k0, s_v0);
+        if (k + 1 >= nch) break;
+        fcommit(s_k1, s_v1);
+        __syncthreads();                               // chunk k+1 in stage 1; stage 0 is free
+        if (k + 2 < nch) fload(k + 2);
+        compute(k + 1, s_k1, s_v1);
+        if (k + 2 < nch) fcommit(s_k0, s_v0);
+      }
+      continue;
+    }
     dma(0, s_k0, s_v0);
     for (int k = 0; k < nch; k += 2) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);       // this wave's part of chunk k has landed
@@ -362,7 +417,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int q = 4 * g4 + r;
       const float lr = lsum[u][r];
-      const float inv = lr == 0.f ? 0.f : __builtin_amdgcn_rcpf(lr);
+      float inv = lr == 0.f ? 0.f : __builtin_amdgcn_rcpf(lr);
+      if constexpr (kF8) inv *= a.v_scale;     // the tiles held V codes
       if (q < srows[u]) {
         const size_t rowbase = ((size_t)(q0 + r0 + wr0 + 16 * u + q) * H + h) * D;
 #pragma unroll
@@ -375,12 +431,12 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int DT, int D>
+template <int DT, int KT, int D>
 hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   const long n = (long)a.num_seqs * a.num_heads * a.num_tiles;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<DT, D>), dim3((unsigned)n), dim3(kPfWaves * 64), 0, stream,
-                     a);
+  hipLaunchKernelGGL((prefill_kernel<DT, KT, D>), dim3((unsigned)n), dim3(kPfWaves * 64), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -388,12 +444,18 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
 
 int prefill_rows_per_tile() { return kRows; }
 
-hipError_t launch_prefill(const PrefillArgs &a, int dt, hipStream_t stream) {
-  switch (dt * 1000 + a.head_dim) {
-    case kF16 * 1000 + 64: return launch_prefill_t<kF16, 64>(a, stream);
-    case kF16 * 1000 + 128: return launch_prefill_t<kF16, 128>(a, stream);
-    case kBF16 * 1000 + 64: return launch_prefill_t<kBF16, 64>(a, stream);
-    case kBF16 * 1000 + 128: return launch_prefill_t<kBF16, 128>(a, stream);
+hipError_t launch_prefill(const PrefillArgs &a, int dt, int kv_dt, hipStream_t stream) {
+  const bool f8 = kv_dt == kFP8;
+  if (!f8 && kv_dt != dt) return hipErrorInvalidValue;
+  switch (dt * 1000 + a.head_dim + (f8 ? 1 : 0)) {
+    case kF16 * 1000 + 64: return launch_prefill_t<kF16, kF16, 64>(a, stream);
+    case kF16 * 1000 + 128: return launch_prefill_t<kF16, kF16, 128>(a, stream);
+    case kBF16 * 1000 + 64: return launch_prefill_t<kBF16, kBF16, 64>(a, stream);
+    case kBF16 * 1000 + 128: return launch_prefill_t<kBF16, kBF16, 128>(a, stream);
+    case kF16 * 1000 + 65: return launch_prefill_t<kF16, kFP8, 64>(a, stream);
+    case kF16 * 1000 + 129: return launch_prefill_t<kF16, kFP8, 128>(a, stream);
+    case kBF16 * 1000 + 65: return launch_prefill_t<kBF16, kFP8, 64>(a, stream);
+    case kBF16 * 1000 + 129: return launch_prefill_t<kBF16, kFP8, 128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

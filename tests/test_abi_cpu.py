@@ -183,6 +183,26 @@ def test_prefill_rejects(lib):
     assert call(mq=0, q=None, out=None) == _capi.PA_OK
 
 
+def test_prefill_fp8_rejects(lib):
+    def call(**kw):
+        a = dict(out=_p(), q=_p(), k=_p(), v=_p(), bt=_p(), cl=_p(), qs=_p(), S=2, T=40, H=8,
+                 Hkv=2, D=128, B=16, NB=64, MB=8, mq=32, maxctx=128, scale=0.1, ks=0.5, vs=0.5,
+                 dt=F16)
+        a.update(kw)
+        return lib.pa_prefill_fp8(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"],
+                                  a["S"], a["T"], a["H"], a["Hkv"], a["D"], a["B"], a["NB"],
+                                  a["MB"], a["mq"], a["maxctx"], a["scale"], a["ks"], a["vs"],
+                                  a["dt"], None)
+    assert call(dt=F32) == _capi.PA_ERR_UNSUPPORTED
+    assert call(dt=_capi.PA_FP8_E4M3) == _capi.PA_ERR_UNSUPPORTED
+    assert call(ks=0.0) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(vs=float("inf")) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(ks=-1.0) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(maxctx=200) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(q=_p(260)) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert call(T=0, q=None, out=None) == _capi.PA_OK
+
+
 def test_copy_blocks_rejects(lib):
     cb = lib.pa_copy_blocks
     assert cb(_p(), None, _p(), None, _p(), -1, 4096, 8, 8, None) == _capi.PA_ERR_INVALID_ARGUMENT

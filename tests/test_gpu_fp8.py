@@ -182,3 +182,41 @@ def test_append_decode_fp8_matches_oracle(name, kw, qt):
         BD.assert_close(got, ref, qt, f"{name} P={ps}")
         assert np.array_equal(from_torch(dev.key_cache, "fp8"), kc), f"{name} P={ps}: K codes"
         assert np.array_equal(from_torch(dev.value_cache, "fp8"), vc), f"{name} P={ps}: V codes"
+
+
+# ---------------------------------------------------------------------------
+# prefill over E4M3 pools
+# ---------------------------------------------------------------------------
+
+PF8_CASES = [
+    ("fresh_mha_d128_b16", dict(ctx=[1, 16, 17, 100, 45], qlens=None, H=4, Hkv=4, D=128, B=16)),
+    ("fresh_gqa_d64_b32", dict(ctx=[70, 33], qlens=None, H=8, Hkv=2, D=64, B=32)),
+    ("suffix_mha_b64", dict(ctx=[200, 64, 300, 5], qlens=[37, 1, 64, 5], H=2, Hkv=2, D=128, B=64)),
+    ("suffix_gqa_long", dict(ctx=[600, 4200], qlens=[300, 40], H=4, Hkv=1, D=128, B=16)),
+]
+
+
+@pytest.mark.parametrize("qt", ["f16", "bf16"])
+@pytest.mark.parametrize("name,kw", PF8_CASES, ids=[c[0] for c in PF8_CASES])
+def test_prefill_fp8_matches_oracle(name, kw, qt):
+    """pa_prefill_fp8 against the oracle's paged_prefill_fp8: codes widened
+    in the kernel, K scale in the score scale, V scale on the output."""
+    ctx, H, Hkv, D, B = kw["ctx"], kw["H"], kw["Hkv"], kw["D"], kw["B"]
+    qlens = kw["qlens"] or ctx
+    _say(f"prefill fp8 {name} {qt}")
+    wl = build("pf8", qt, ctx, H, Hkv, D, B, seed=97 + D + B, pool="choice", pool_factor=1.3,
+               kv_dtype="fp8", kv_scale=0.5)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = normal_array(98, 40, (int(qs[-1]), H, D), qt, 0.5)
+    tdt = torch.float16 if qt == "f16" else torch.bfloat16
+    out = torch.full((int(qs[-1]), H, D), float("inf"), dtype=tdt, device="cuda")
+    pa.pa_prefill_fp8(out, to_torch(q, qt, "cuda"), to_torch(wl.key_cache, "fp8", "cuda"),
+                      to_torch(wl.value_cache, "fp8", "cuda"),
+                      torch.tensor(wl.block_tables, device="cuda"),
+                      torch.tensor(wl.context_lens, device="cuda"), torch.tensor(qs, device="cuda"),
+                      int(max(qlens)), wl.max_context_len, wl.k_scale, wl.v_scale, wl.scale)
+    torch.cuda.synchronize()
+    got = P.to_f64(from_torch(out, qt), qt)
+    ref = P.paged_prefill_fp8(q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens,
+                              qs, B, wl.scale, qt, wl.k_scale, wl.v_scale, Hkv)
+    BD.assert_close(got, ref, qt, f"prefill fp8 {name} {qt}")

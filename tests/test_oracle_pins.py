@@ -589,3 +589,52 @@ def test_pin_prefill_last_row_is_decode():
     last = q[qs[1:] - 1]                                        # [S][H][D]
     dec = P.paged_decode(last, kc, vc, tables, cl, B, 0.3, "f32")
     assert np.array_equal(got[qs[1:] - 1], dec)
+
+
+def _fp8_prefill_case(seed, ctx, qlens, H, Hkv, D, B):
+    from workloads import e4m3_codes, normal_array
+    rng = np.random.default_rng(seed)
+    nblk = [-(-c // B) for c in ctx]
+    NB = sum(nblk) + 3
+    ids = rng.permutation(NB)
+    tables = np.full((len(ctx), max(nblk)), -1, np.int32)
+    k = 0
+    for s, n in enumerate(nblk):
+        tables[s, :n] = ids[k:k + n]
+        k += n
+    kc = e4m3_codes(seed, 1, (NB, Hkv, B, D))
+    vc = e4m3_codes(seed, 2, (NB, Hkv, B, D))
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = normal_array(seed, 3, (int(qs[-1]), H, D), "f16")
+    return kc, vc, tables, np.array(ctx, np.int32), qs, q
+
+
+def test_pin_prefill_fp8_is_prefill_over_the_decoded_pools():
+    """Prefill over E4M3 pools equals prefill over float32 pools holding
+    decode(code) * scale (exact: E4M3 values times a power of two are
+    float32 values) with the fp16 queries widened exactly: the codes are
+    gathered through the table at the causal positions and scaled per pool."""
+    B, H, Hkv, D = 4, 4, 2, 8
+    ctx, qlens = [11, 30, 5], [3, 30, 5]
+    kc, vc, tables, cl, qs, q = _fp8_prefill_case(61, ctx, qlens, H, Hkv, D, B)
+    ks, vs = 0.5, 0.25
+    got = P.paged_prefill_fp8(q, kc, vc, tables, cl, qs, B, 0.3, "f16", ks, vs, Hkv)
+    kf = (P.e4m3_decode(kc) * ks).astype(np.float32)
+    vf = (P.e4m3_decode(vc) * vs).astype(np.float32)
+    assert np.array_equal(kf.astype(np.float64), P.e4m3_decode(kc) * ks)
+    q32 = P.to_f64(q, "f16").astype(np.float32)
+    ref = P.paged_prefill(q32, kf, vf, tables, cl, qs, B, 0.3, "f32", Hkv)
+    assert np.array_equal(got, ref)
+    # the K scale acts as a factor of the score scale
+    got2 = P.paged_prefill_fp8(q, kc, vc, tables, cl, qs, B, 0.15, "f16", 2 * ks, vs, Hkv)
+    assert np.allclose(got2, got, rtol=0, atol=1e-12)
+
+
+def test_pin_prefill_fp8_last_row_is_fp8_decode():
+    B, H, Hkv, D = 4, 4, 4, 8
+    ctx, qlens = [9, 22], [4, 22]
+    kc, vc, tables, cl, qs, q = _fp8_prefill_case(62, ctx, qlens, H, Hkv, D, B)
+    got = P.paged_prefill_fp8(q, kc, vc, tables, cl, qs, B, 0.3, "f16", 0.5, 0.5)
+    last = q[qs[1:] - 1]
+    dec = P.paged_decode_fp8(last, kc, vc, tables, cl, B, 0.3, "f16", 0.5, 0.5)
+    assert np.array_equal(got[qs[1:] - 1], dec)
