@@ -53,48 +53,45 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
     "llama7b_f16/B16/P4096/append": {
-        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
-        "fetch_kib": 328576.391, "fetch_scale": 1048576 / 524319.250,
-        "write_kib": 768.0, "write_scale": 1.0,
-        "profile": "profiles/decode_mha_llama7b_f16.md"},
-    # decode_gqa_kernel + merge_kernel
+        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
+        "fetch_kib": 328576.453, "fetch_scale": 1048576 / 524315.062,
+        "write_kib": 768.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
     "gqa70b_bf16/B16/P2048/append": {
-        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
-        "fetch_kib": 103368.812 + 601.500, "fetch_scale": 1048576 / 524307.188,
-        "write_kib": 1104.188 + 256.0, "write_scale": 1.0,
-        "profile": "profiles/decode_gqa_gqa70b_bf16.md"},
+        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
+        "fetch_kib": 103368.062 + 601.500, "fetch_scale": 1048576 / 524306.875,
+        "write_kib": 1104.094 + 256.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
     "llama7b_fp8kv/B16/P4096/append": {
-        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
-        "fetch_kib": 154700.641, "fetch_scale": 1048576 / 524307.500,
-        "write_kib": 512.0, "write_scale": 1.0,
-        "profile": "profiles/decode_fp8_llama7b_fp8kv.md"},
-    "llama13b_bf16/B16/P4096/append": {
-        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
-        "fetch_kib": 1311908.150, "fetch_scale": 1048576 / 524320.000,
-        "write_kib": 1920.0, "write_scale": 1.0,
-        "profile": "profiles/decode_mha_llama13b_bf16.md"},
-    "llama13b_bf16/B32/P4096/append": {
-        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
-        "fetch_kib": 1311845.725, "fetch_scale": 1048576 / 524319.400,
-        "write_kib": 1920.0, "write_scale": 1.0,
-        "profile": "profiles/decode_mha_llama13b_bf16.md"},
-    "llama13b_bf16/B64/P4096/append": {
-        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
-        "fetch_kib": 1311811.725, "fetch_scale": 1048576 / 524307.200,
-        "write_kib": 1920.0, "write_scale": 1.0,
-        "profile": "profiles/decode_mha_llama13b_bf16.md"},
-    # decode_mha_kernel + merge_kernel; the shared prefix is fetched once
-    "longctx_prefix_f16/B64/P512/append": {
-        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
-        "fetch_kib": 1984767.100 + 4249.050, "fetch_scale": 1048576 / 524318.600,
-        "write_kib": 9344.0 + 64.0, "write_scale": 1.0,
-        "profile": "profiles/decode_mha_longctx_prefix_f16.md"},
-    # decode_gqa_kernel over E4M3 pools + merge_kernel
+        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
+        "fetch_kib": 154700.281, "fetch_scale": 1048576 / 524307.312,
+        "write_kib": 512.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
     "gqa70b_fp8kv/B16/P1024/append": {
-        "sources": "4199b49ff5e1a7c3dd9454918e7a310cd9a2da02f09ac9fbaef7eb2317e2308d",
-        "fetch_kib": 49056.250 + 969.500, "fetch_scale": 1048576 / 524307.625,
-        "write_kib": 1824.000 + 256.0, "write_scale": 1.0,
-        "profile": "profiles/decode_gqa_fp8_gqa70b_fp8kv.md"},
+        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
+        "fetch_kib": 49056.328 + 969.500, "fetch_scale": 1048576 / 524306.875,
+        "write_kib": 1824.062 + 256.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
+    "llama13b_bf16/B16/P4096/append": {
+        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
+        "fetch_kib": 1311912.984, "fetch_scale": 1048576 / 524310.750,
+        "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
+    "llama13b_bf16/B32/P4096/append": {
+        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
+        "fetch_kib": 1311845.578, "fetch_scale": 1048576 / 524306.938,
+        "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
+    "llama13b_bf16/B64/P4096/append": {
+        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
+        "fetch_kib": 1311812.031, "fetch_scale": 1048576 / 524307.062,
+        "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
+    "longctx_prefix_f16/B64/P512/append": {
+        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
+        "fetch_kib": 1985073.734 + 4249.062, "fetch_scale": 1048576 / 524318.750,
+        "write_kib": 9344.000 + 64.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
 }
 
 
