@@ -8,20 +8,29 @@ in one launch (plus the log-sum-exp merge launch when partitions split a
 context); ``--step three`` times the same step as pa_compute_slots +
 pa_cache_write(_fp8) + pa_decode(_fp8).
 
-Prints ONE JSON line.  ``value`` is context tokens per second (sum of
-context_lens over a step / step time) with every input already in HBM.
-``roofline`` rates the decode launch: algorithmic bytes (K and V of every
-context token, q, out, and the used block-table entries) over its mean
-duration, measured with HIP events on the stream the kernels run on (around
-runs of five timed steps, or every fifth decode call of the three-call
-step), against the MI355X HBM peak of 8 TB/s.  ``cpu_baseline`` times the float64 oracle on
-a bounded sample of the same workload on this host.
+Prints ONE JSON line.  By default the line is the largest workload that fits
+one GPU: 8 sequences of 32,768 tokens (LLaMA-7B-shaped heads, fp16, blocks of
+64) whose first 2048 tokens are one shared prefix, in 512-token partitions.
+Every other workload (the tiny fp32 case, the LLaMA-7B layer, the LLaMA-13B
+layer at block sizes 16/32/64, the 70B-style grouped-query share, and the
+LLaMA-7B and grouped-query shapes over E4M3 pools) is timed in the same run
+and reported under ``sub_records``, each with its own roofline.
+
+``value`` is context tokens per second (sum of context_lens over a step / step
+time) with every input already in HBM.  ``roofline`` rates the decode launch:
+algorithmic bytes (K and V of every context token, q, out, and the used
+block-table entries) over its mean duration, measured with HIP events on the
+stream the kernels run on (around runs of five timed steps, or every fifth
+decode call of the three-call step), against the MI355X HBM peak of 8 TB/s.
+``cpu_baseline`` times the float64 oracle on a bounded sample of the same
+workload on this host's cores, before the GPU is touched.
 
 Pools are rotated between steps (several resident copies, each larger than
 the 256 MB last-level cache together with its neighbours), so a step never
 finds the previous step's K/V in cache.
 
-    python bench.py [--steps K] [--warmup W] [--config 1] [--partition-size P]
+    python bench.py [--steps K] [--warmup W] [--config N] [--sub-configs LIST]
+    python bench.py --op {prefill,cache_write,copy_blocks,block_manager}
 """
 from __future__ import annotations
 
@@ -156,55 +165,27 @@ def measured_traffic(workload: str, block_size: int, partition_size: int, fused:
     return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024
 
 
-def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
-    """The float64 oracle as it stands, single-threaded, on (sequence, head)
-    pairs in order, passing over the workload again while less than
-    ``budget_s`` has been spent."""
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:                                    # pragma: no cover
-        threadpool_limits = None
-    import oracle.paged as P
 
-    pairs = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_heads)]
-    done, tokens = 0, 0
-    ctx_mgr = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx_mgr:
-        ctx_mgr.__enter__()
-    try:
-        t0 = time.perf_counter()
-        for s, h in pairs * 1000:
-            if wl.pool_dtype == "fp8":
-                P.paged_decode_fp8(wl.q, wl.key_cache, wl.value_cache, wl.block_tables,
-                                   wl.context_lens, wl.block_size, wl.scale, wl.dtype,
-                                   wl.k_scale, wl.v_scale, wl.num_kv_heads, pairs=[(s, h)])
-            else:
-                P.paged_decode(wl.q, wl.key_cache, wl.value_cache, wl.block_tables,
-                               wl.context_lens, wl.block_size, wl.scale, wl.dtype,
-                               wl.num_kv_heads, pairs=[(s, h)])
-            done += 1
-            tokens += int(wl.context_lens[s])
-            if time.perf_counter() - t0 > budget_s:
-                break
-        el = time.perf_counter() - t0
-    finally:
-        if ctx_mgr:
-            ctx_mgr.__exit__(None, None, None)
-    # one context token of the metric covers all H query heads
-    rate = tokens / wl.num_heads / el
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {"value": rate, "unit": "context tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} (sequence, head) pairs in order over the workload's {len(pairs)} "
-                      f"({done / len(pairs):.2f} passes), {tokens} head-tokens in {el:.1f} s, "
-                      f"float64 numpy, 1 thread on {cpu}"}
+# ---------------------------------------------------------------------------
+# The oracle on the host's cores.  Every CPU baseline runs the oracle as it
+# stands, one work item per call, in a pool of forked worker processes (one
+# BLAS thread each), before anything in this process has initialised the GPU:
+# forking a process that holds GPU state is not safe.
+# ---------------------------------------------------------------------------
+
+_ORACLE_STATE = {}          # what the forked workers read (set before the fork)
+MAX_HOST_WORKERS = 16       # a one-GPU machine's share of its host's cores
+
+
+def host_workers() -> tuple[int, int]:
+    """(workers to use, cores this process may run on): the affinity set,
+    capped at OMP_NUM_THREADS when that is set and at MAX_HOST_WORKERS."""
+    aff = len(os.sched_getaffinity(0))
+    n = min(aff, MAX_HOST_WORKERS)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n), aff
 
 
 def _cpu_name() -> str:
@@ -218,28 +199,431 @@ def _cpu_name() -> str:
     return "unknown"
 
 
-def _timed_oracle(fn, items, budget_s: float):
-    """Run ``fn(item)`` over ``items`` in order, single-threaded, until the
-    time budget is spent; returns (items done, seconds)."""
+def _worker_init() -> None:
+    """One BLAS thread per worker; arrays the oracle writes (named in
+    ``_ORACLE_STATE["private"]``) become private, touched copies before the
+    timed region, so no copy-on-write fault lands inside it."""
     try:
         from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
     except ImportError:                                    # pragma: no cover
-        threadpool_limits = None
-    ctx_mgr = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx_mgr:
-        ctx_mgr.__enter__()
+        pass
+    for k in _ORACLE_STATE.get("private", ()):
+        _ORACLE_STATE[k] = _ORACLE_STATE[k].copy()
+
+
+def _run_item(item):
+    """One oracle work item in a worker: returns what it counts toward the
+    rate (tokens, bytes, ...)."""
+    return _ORACLE_STATE["fn"](item)
+
+
+def parallel_oracle(fn, items, budget_s: float) -> dict:
+    """Run ``fn(item)`` over ``items`` (cycled) on the host's cores until
+    ``budget_s`` of wall time is spent; ``fn`` returns the item's count.
+    Returns the items done, the summed count, the wall seconds, the workers
+    and the affinity core count."""
+    import itertools
+    import multiprocessing as mp
+
+    workers, aff = host_workers()
+    _ORACLE_STATE["fn"] = fn
+    it = itertools.cycle(items)
+    done = acc = 0
+    batch = workers * 2
     try:
-        done = 0
-        t0 = time.perf_counter()
-        for it in items:
-            fn(it)
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        return done, time.perf_counter() - t0
+        with mp.get_context("fork").Pool(workers, initializer=_worker_init) as pool:
+            pool.map(_run_item, [items[0]] * workers, chunksize=1)     # start every worker
+            t0 = time.perf_counter()
+            while True:
+                b0 = time.perf_counter()
+                chunk = [next(it) for _ in range(batch)]
+                acc += sum(pool.map(_run_item, chunk, chunksize=1))
+                done += len(chunk)
+                now = time.perf_counter()
+                if now - t0 > budget_s:
+                    break
+                if now - b0 < 0.25:
+                    batch *= 2
+            el = time.perf_counter() - t0
     finally:
-        if ctx_mgr:
-            ctx_mgr.__exit__(None, None, None)
+        _ORACLE_STATE.clear()
+    return {"items": done, "count": acc, "seconds": el, "workers": workers, "affinity": aff}
+
+
+def _oracle_record(value, unit, run, what) -> dict:
+    return {"value": value, "unit": unit, "cores": run["workers"], "kind": "oracle",
+            "sample": f"{what}; {run['workers']} worker processes (1 BLAS thread each; "
+                      f"{run['affinity']} cores in this process's affinity set) for "
+                      f"{run['seconds']:.1f} s on {_cpu_name()}"}
+
+
+def _decode_pair(item):
+    import oracle.paged as P
+    wl = _ORACLE_STATE["wl"]
+    s, h = item
+    if wl.pool_dtype == "fp8":
+        P.paged_decode_fp8(wl.q, wl.key_cache, wl.value_cache, wl.block_tables,
+                           wl.context_lens, wl.block_size, wl.scale, wl.dtype,
+                           wl.k_scale, wl.v_scale, wl.num_kv_heads, pairs=[(s, h)])
+    else:
+        P.paged_decode(wl.q, wl.key_cache, wl.value_cache, wl.block_tables,
+                       wl.context_lens, wl.block_size, wl.scale, wl.dtype,
+                       wl.num_kv_heads, pairs=[(s, h)])
+    return int(wl.context_lens[s])
+
+
+def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+    """The float64 oracle as it stands on the workload's (sequence, head)
+    pairs in order, cycled until ``budget_s`` is spent, on the host's cores;
+    reported as context tokens/s (one context token covers all H heads)."""
+    _ORACLE_STATE["wl"] = wl
+    pairs = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_heads)]
+    try:
+        run = parallel_oracle(_decode_pair, pairs, budget_s)
+    finally:
+        _ORACLE_STATE.pop("wl", None)
+    rate = run["count"] / wl.num_heads / run["seconds"]
+    what = (f"{run['items']} (sequence, head) pairs of {wl.name} in order over its "
+            f"{len(pairs)} ({run['items'] / len(pairs):.2f} passes), {run['count']} head-tokens, "
+            f"float64 numpy")
+    return _oracle_record(rate, "context tokens/s", run, what)
+
+
+# ---------------------------------------------------------------------------
+# Decode (the headline): one step = pa_append_decode(_fp8), or the three-call
+# step, over one batch of the workload.
+# ---------------------------------------------------------------------------
+
+# The largest workload that fits one GPU, timed by default: 8 sequences of
+# 32,768 tokens sharing a 2048-token prefix, split into 512-token partitions.
+HEADLINE_CONFIG = 4
+# Timed in the same run as sub-records: workload[:block size].
+SUB_CONFIGS = "0,1,2:16,2:32,2:64,3,5,6"
+
+
+def parse_sub_configs(spec: str) -> list:
+    out = []
+    for part in (p.strip() for p in spec.split(",") if p.strip()):
+        idx, _, b = part.partition(":")
+        out.append((int(idx), int(b) if b else None))
+    return out
+
+
+class ReadProbe:
+    """pa_read_probe over one 2 GiB device buffer: the achievable read rate
+    in index order, as random 4 KB tiles, and as a call's own tiles over as
+    many bytes as its K and V."""
+
+    def __init__(self, torch, pa):
+        self.torch, self.pa = torch, pa
+        self.big = torch.ones(1 << 29, dtype=torch.int32, device="cuda")
+        self.sink = torch.empty(pa.PA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+
+    def best_gbps(self, buf, tile, order, reps=5) -> float:
+        torch, pa = self.torch, self.pa
+        stream = torch.cuda.current_stream()
+        pa.pa_read_probe(buf, tile, order, self.sink)
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pa.pa_read_probe(buf, tile, order, self.sink)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / 1e3)
+        return buf.numel() * 4 / best / 1e9
+
+    def same_bytes(self, kv_bytes: int, tile: int) -> float:
+        torch = self.torch
+        n = max(1, min(kv_bytes // tile, self.big.numel() * 4 // tile))
+        perm = torch.randperm(n, device="cuda",
+                              generator=torch.Generator(device="cuda").manual_seed(1)).int()
+        return self.best_gbps(self.big[:n * tile // 4], tile, perm)
+
+    def full(self, kv_bytes: int, tile: int) -> dict:
+        torch = self.torch
+        perm = torch.randperm(self.big.numel() * 4 // 4096, device="cuda",
+                              generator=torch.Generator(device="cuda").manual_seed(0)).int()
+        return {"how": "pa_read_probe, best of 5 HIP-event-timed calls: 2 GiB in index "
+                       "order, 2 GiB as random 4 KB tiles, the call's K+V bytes as its own "
+                       "tiles in random order",
+                "same_bytes_tile_bytes": tile,
+                "contiguous_gbps": self.best_gbps(self.big, 4096, None),
+                "random_4k_tiles_gbps": self.best_gbps(self.big, 4096, perm),
+                "random_tiles_same_bytes_gbps": self.same_bytes(kv_bytes, tile)}
+
+
+def time_decode(wl, args, torch, pa) -> dict:
+    """Time ``args.steps`` decode steps of ``wl`` (after ``args.warmup``
+    untimed ones) with its inputs resident in HBM; returns its record."""
+    from workloads import to_device
+
+    S, H, Hkv, D, B = wl.num_seqs, wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    dt = wl.dtype
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    maxctx = wl.max_context_len
+    fp8 = wl.pool_dtype == "fp8"
+    size_dt = pa.PA_FP8_E4M3 if fp8 else pa.DTYPE_CODES[tdt]
+    lib = pa.load_library()
+    P_used = lib.pa_decode_partition_size(S, H, Hkv, D, B, maxctx, wl.partition_size, size_dt)
+    ws_bytes = lib.pa_decode_workspace_size(S, H, Hkv, D, B, maxctx, wl.partition_size, size_dt)
+    fused = args.step == "fused"
+    nbytes = algorithmic_bytes(wl.context_lens, H, Hkv, D, B, dt, wl.pool_dtype,
+                               new_row_write=fused)
+    sum_ctx = int(wl.context_lens.sum())
+
+    base = to_device(wl)
+    pool_bytes = base.key_cache.numel() * base.key_cache.element_size() * 2
+    # Rotate pool copies so that no step finds the previous one's K/V in the
+    # 256 MB last-level cache.
+    copies = max(2, math.ceil(2 * MALL_BYTES / pool_bytes) + 1)
+    pools = [(base.key_cache, base.value_cache)] + [
+        (base.key_cache.clone(), base.value_cache.clone()) for _ in range(copies - 1)]
+    slots = torch.empty(S, dtype=torch.int64, device="cuda")
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: S={S} H={H}/{Hkv} D={D} B={B} {dt}"
+          f"{' K/V fp8' if fp8 else ''} sum(ctx)={sum_ctx} P={P_used} pool copies={copies} "
+          f"({pool_bytes / 2**20:.0f} MiB each)", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kc, vc = pools[i % copies]
+        if fused:
+            if fp8:
+                pa.pa_append_decode_fp8(base.out, base.q, base.new_key, base.new_value, kc, vc,
+                                        base.block_tables, base.context_lens, maxctx,
+                                        wl.k_scale, wl.v_scale, wl.scale, wl.partition_size,
+                                        workspace)
+            else:
+                pa.pa_append_decode(base.out, base.q, base.new_key, base.new_value, kc, vc,
+                                    base.block_tables, base.context_lens, maxctx, wl.scale,
+                                    wl.partition_size, workspace)
+            return
+        pa.pa_compute_slots(slots, base.block_tables, B, wl.num_blocks,
+                            context_lens=base.context_lens)
+        if fp8:
+            pa.pa_cache_write_fp8(base.new_key, base.new_value, kc, vc, slots, wl.k_scale,
+                                  wl.v_scale)
+        else:
+            pa.pa_cache_write(base.new_key, base.new_value, kc, vc, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        if fp8:
+            pa.pa_decode_fp8(base.out, base.q, kc, vc, base.block_tables, base.context_lens,
+                             maxctx, wl.k_scale, wl.v_scale, wl.scale, wl.partition_size,
+                             workspace)
+        else:
+            pa.pa_decode(base.out, base.q, kc, vc, base.block_tables, base.context_lens, maxctx,
+                         wl.scale, wl.partition_size, workspace)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Launch durations from HIP events on the kernels' stream.  One-launch
+    # steps: an event pair brackets each run of EVENT_EVERY consecutive steps
+    # (launch duration = elapsed / run length), so the events' own cost (~8 us
+    # per pair on a ~105 us LLaMA-7B step) is paid once per run.  Three-call
+    # steps: the pair brackets the decode call of every EVENT_EVERY-th step.
+    # Fewer than 2 * EVENT_EVERY timed steps: every step is measured alone.
+    every = EVENT_EVERY if args.steps >= 2 * EVENT_EVERY else 1
+    samples = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if fused:
+        for g0 in range(0, args.steps, every):
+            g1 = min(g0 + every, args.steps)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(g0, g1):
+                step(args.warmup + i)
+            e1.record(stream)
+            samples.append((e0, e1, g1 - g0))
+    else:
+        for i in range(args.steps):
+            if i % every == 0:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                samples.append((ev[0], ev[1], 1))
+                step(args.warmup + i, ev)
+            else:
+                step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = sorted(e0.elapsed_time(e1) / n for e0, e1, n in samples)
+    dec_mean_s = sum(dec_ms) / len(dec_ms) / 1e3
+    dec_med_s = dec_ms[len(dec_ms) // 2] / 1e3
+    print(f"[bench] {wl.name}: {args.steps} steps in {wall * 1e3:.2f} ms; decode mean "
+          f"{dec_mean_s * 1e6:.1f} us median {dec_med_s * 1e6:.1f} us p10 "
+          f"{dec_ms[len(dec_ms) // 10] * 1e3:.1f} us p90 "
+          f"{dec_ms[(9 * len(dec_ms)) // 10] * 1e3:.1f} us", file=sys.stderr, flush=True)
+    del pools, base, workspace, slots
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    achieved = nbytes["total"] / dec_mean_s / 1e9
+    # which kernels the library dispatches to (for the record's label only)
+    gqa = wl.pool_dtype in ("f16", "bf16", "fp8") and H // Hkv >= 2
+    kernels = ("decode_gqa_kernel" if gqa else "decode_mha_kernel") + (
+        " + merge_kernel" if P_used < maxctx else "")
+    return {
+        "workload": wl.name,
+        "value": sum_ctx * args.steps / wall,
+        "unit": "context tokens/s",
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "dtype": dt if not fp8 else f"{dt} (K/V fp8 e4m3)",
+        "config": {"workload": wl.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": B, "sum_context_tokens": sum_ctx,
+                   "max_context_len": maxctx, "partition_size": P_used, "seed": wl.seed,
+                   "pool_copies_rotated": copies,
+                   "step": ("pa_append_decode(_fp8): slot, K/V write and attention in one "
+                            "launch" if fused else "pa_compute_slots + pa_cache_write(_fp8) + "
+                            "pa_decode(_fp8)")},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(wl.name, B, P_used, fused),
+                     "kernel": ("pa_append_decode" if fused else "pa_decode") +
+                               ("_fp8" if fp8 else "") + f" ({kernels})",
+                     "bytes_per_launch": nbytes["total"], "mean_launch_us": dec_mean_s * 1e6,
+                     "median_launch_us": dec_med_s * 1e6, "event_samples": len(dec_ms),
+                     "launches_per_sample": every if fused else 1,
+                     "p10_launch_us": dec_ms[len(dec_ms) // 10] * 1e3,
+                     "p90_launch_us": dec_ms[(9 * len(dec_ms)) // 10] * 1e3},
+        "decode_context_tokens_per_s": sum_ctx / dec_mean_s,
+        "_kv_bytes": nbytes["kv"],
+        "_tile_bytes": max(1024, B * D * ELEM[wl.pool_dtype or dt]),
+    }
+
+
+def bench_decode(args) -> dict:
+    """The headline line (one workload, by default the long-context one) and
+    the sub-records of the other workloads, timed in one run."""
+    from workloads import make_workload
+
+    head_idx = HEADLINE_CONFIG if args.config is None else args.config
+    subs = []
+    if args.sub_configs is not None:
+        subs = parse_sub_configs(args.sub_configs)
+    elif args.config is None:
+        subs = parse_sub_configs(SUB_CONFIGS)
+    print(f"[bench] building workload {head_idx}", file=sys.stderr, flush=True)
+    wl = make_workload(head_idx, seed=args.seed, block_size=args.block_size)
+    if args.partition_size is not None:
+        wl.partition_size = args.partition_size
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before this process touches the GPU (the oracle runs in forked workers)
+        print(f"[bench] timing the float64 oracle on the host ({host_workers()[0]} workers)",
+              file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl)
+
+    import torch
+
+    import paged_kv_cache_368_amd as pa
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pa.load_library()
+    dev_name = torch.cuda.get_device_name(0)
+    print(f"[bench] device {dev_name}", file=sys.stderr, flush=True)
+    head = time_decode(wl, args, torch, pa)
+    del wl
+    probe = None
+    ceiling = None
+    if not args.no_ceiling:
+        probe = ReadProbe(torch, pa)
+        ceiling = probe.full(head["_kv_bytes"], head["_tile_bytes"])
+
+    records = []
+    for idx, b in subs:
+        print(f"[bench] building workload {idx}" + (f" (B={b})" if b else ""), file=sys.stderr,
+              flush=True)
+        swl = make_workload(idx, block_size=b)
+        rec = time_decode(swl, args, torch, pa)
+        del swl
+        if probe is not None:
+            rec["random_tiles_same_bytes_gbps"] = probe.same_bytes(rec["_kv_bytes"],
+                                                                   rec["_tile_bytes"])
+            rec["frac_of_same_bytes_tile_ceiling"] = (rec["roofline"]["achieved"] /
+                                                      rec["random_tiles_same_bytes_gbps"])
+        for k in ("_kv_bytes", "_tile_bytes"):
+            rec.pop(k)
+        records.append(rec)
+    if probe is not None:
+        del probe
+        torch.cuda.synchronize()
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    achieved = head["roofline"]["achieved"]
+    result = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic (seeded N(0,1) K/V/q, random block tables; no dataset)",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "read_ceiling": ceiling,
+        "frac_of_tile_ceiling": (achieved / ceiling["random_4k_tiles_gbps"]) if ceiling else None,
+        "frac_of_same_bytes_tile_ceiling":
+            (achieved / ceiling["random_tiles_same_bytes_gbps"]) if ceiling else None,
+        "decode_context_tokens_per_s": head["decode_context_tokens_per_s"],
+        "device": dev_name,
+        "cpu_baseline": cpu,
+        "sub_records": records,
+    }
+    return result
+
+
+# ---------------------------------------------------------------------------
+# Other ops, each on its own line (--op ...)
+# ---------------------------------------------------------------------------
+
+def _copy_item(pair):
+    import oracle.paged as P
+    kc, vc = _ORACLE_STATE["kc"], _ORACLE_STATE["vc"]
+    P.copy_blocks(kc, kc, [pair])
+    P.copy_blocks(vc, vc, [pair])
+    return 2 * 2 * kc[0].nbytes                  # read + write, K and V
+
+
+def _copy_cpu_baseline(Hkv, B, D, npairs) -> dict:
+    """The oracle's block copy on host pools of the same block shape: copy
+    on write of a random pairing's pairs, bytes read + written."""
+    import numpy as np
+
+    NB = 2 * npairs
+    rng = np.random.default_rng(11)
+    _ORACLE_STATE["kc"] = rng.integers(0, 65535, (NB, Hkv, B, D), dtype=np.uint16)
+    _ORACLE_STATE["vc"] = rng.integers(0, 65535, (NB, Hkv, B, D), dtype=np.uint16)
+    _ORACLE_STATE["private"] = ("kc", "vc")
+    perm = rng.permutation(NB)
+    pairs = list(zip(perm[:npairs].tolist(), perm[npairs:].tolist()))
+    try:
+        run = parallel_oracle(_copy_item, pairs, 10.0)
+    finally:
+        for k in ("kc", "vc", "private"):
+            _ORACLE_STATE.pop(k, None)
+    return _oracle_record(run["count"] / run["seconds"] / 1e9, "GB/s (read+write)", run,
+                          f"{run['items']} block pairs of {npairs} (K and V), numpy")
 
 
 def bench_copy_blocks(args) -> dict:
@@ -248,11 +632,15 @@ def bench_copy_blocks(args) -> dict:
     copy on write of --pairs random blocks inside the device pools, and a
     swap of the same number of blocks out to pinned host memory and back.
     Bytes = read + write of both pools."""
+    Hkv, B, D, npairs = 40, 16, 128, args.pairs
+    # the host sample: 512 pairs over 1024 blocks per pool (each worker holds
+    # its own copy of the pools it writes)
+    cpu = None if args.no_cpu_baseline else _copy_cpu_baseline(Hkv, B, D, min(npairs, 512))
+
     import torch
 
     import paged_kv_cache_368_amd as pa
-
-    Hkv, B, D, npairs = 40, 16, 128, args.pairs
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
     NB = max(4 * npairs, 8192)
     block_bytes = Hkv * B * D * 2
     g = torch.Generator().manual_seed(11)
@@ -295,35 +683,41 @@ def bench_copy_blocks(args) -> dict:
                    "head_dim": D, "pairs": npairs, "block_bytes": block_bytes},
         "roofline": {"bound": "hbm", "achieved": moved / t_cow / 1e9, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": moved / t_cow / 1e9 / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "copy_blocks_kernel (copy on write)"},
+                     "kernel": "copy_blocks_kernel (copy on write)", "bytes_per_launch": moved,
+                     "mean_launch_us": t_cow * 1e6},
         "swap_out_gbps": one_way / t_out / 1e9, "swap_in_gbps": one_way / t_in / 1e9,
         "swap_out_us": t_out * 1e6, "swap_in_us": t_in * 1e6,
-        "cpu_baseline": None if args.no_cpu_baseline else _copy_cpu_baseline(Hkv, B, D, npairs),
+        "cpu_baseline": cpu,
     }
 
 
-def _copy_cpu_baseline(Hkv, B, D, npairs) -> dict:
-    """The oracle's block copy on host pools of the same block shape: copy
-    on write of the first pairs of a random pairing, bytes read + written."""
+def _cache_write_item(i):
+    import oracle.paged as P
+    st = _ORACLE_STATE
+    P.cache_write(st["kc"], st["vc"], st["key"][i:i + 1], st["val"][i:i + 1],
+                  st["slots"][i:i + 1], st["B"])
+    return 2 * 2 * st["key"][i].nbytes            # K and V rows read + written
+
+
+def _cache_write_cpu_baseline(Hkv, B, D) -> dict:
+    """The oracle's cache write, one token per call, into host pools of the
+    same row shape (1024 blocks) at distinct random slots."""
     import numpy as np
 
-    import oracle.paged as P
-
-    NB = 2 * npairs
-    rng = np.random.default_rng(11)
-    kc = rng.integers(0, 65535, (NB, Hkv, B, D), dtype=np.uint16)
-    vc = rng.integers(0, 65535, (NB, Hkv, B, D), dtype=np.uint16)
-    perm = rng.permutation(NB)
-    pairs = list(zip(perm[:npairs].tolist(), perm[npairs:].tolist()))
-
-    def one(pair):
-        P.copy_blocks(kc, kc, [pair])
-        P.copy_blocks(vc, vc, [pair])
-
-    done, el = _timed_oracle(one, pairs, 10.0)
-    moved = 2 * 2 * done * Hkv * B * D * 2
-    return {"value": moved / el / 1e9, "unit": "GB/s (read+write)", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {npairs} block pairs (K and V), numpy, 1 thread on {_cpu_name()}"}
+    NB, T = 1024, 16384
+    rng = np.random.default_rng(12)
+    _ORACLE_STATE.update(
+        kc=np.zeros((NB, Hkv, B, D), dtype=np.uint16), vc=np.zeros((NB, Hkv, B, D), dtype=np.uint16),
+        key=rng.integers(0, 65535, (T, Hkv, D), dtype=np.uint16),
+        val=rng.integers(0, 65535, (T, Hkv, D), dtype=np.uint16),
+        slots=rng.permutation(NB * B)[:T].astype(np.int64), B=B, private=("kc", "vc"))
+    try:
+        run = parallel_oracle(_cache_write_item, list(range(T)), 8.0)
+    finally:
+        for k in ("kc", "vc", "key", "val", "slots", "B", "private"):
+            _ORACLE_STATE.pop(k, None)
+    return _oracle_record(run["count"] / run["seconds"] / 1e9, "GB/s (read+write)", run,
+                          f"{run['items']} tokens (K and V rows, one per call) of {T}, numpy")
 
 
 def bench_cache_write(args) -> dict:
@@ -331,11 +725,13 @@ def bench_cache_write(args) -> dict:
     tokens, 40 kv heads of 128): the K/V rows of a prompt batch (8 x 2048
     tokens, the value: GB/s of rows read + slot bytes written) and of one
     decode step (64 tokens, latency), each into distinct random slots."""
+    Hkv, B, D, NB = 40, 16, 128, 8192
+    cpu = None if args.no_cpu_baseline else _cache_write_cpu_baseline(Hkv, B, D)
+
     import torch
 
     import paged_kv_cache_368_amd as pa
-
-    Hkv, B, D, NB = 40, 16, 128, 8192
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
     g = torch.Generator(device="cuda").manual_seed(12)
     kc = torch.empty((NB, Hkv, B, D), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
     vc = torch.empty_like(kc).normal_(generator=g)
@@ -373,32 +769,8 @@ def bench_cache_write(args) -> dict:
                      "kernel": "cache_write_kernel", "bytes_per_launch": moved,
                      "mean_launch_us": t * 1e6},
         "decode_step_write": {"tokens": Ts, "mean_us": ts * 1e6, "gbps": moved_s / ts / 1e9},
-        "cpu_baseline": None if args.no_cpu_baseline else _cache_write_cpu_baseline(Hkv, B, D),
+        "cpu_baseline": cpu,
     }
-
-
-def _cache_write_cpu_baseline(Hkv, B, D) -> dict:
-    """The oracle's cache write, one token at a time, into host pools of the
-    same row shape (1024 blocks) at distinct random slots, for up to ~8 s."""
-    import numpy as np
-
-    import oracle.paged as P
-
-    NB, T = 1024, 16384
-    rng = np.random.default_rng(12)
-    kc = np.zeros((NB, Hkv, B, D), dtype=np.uint16)
-    vc = np.zeros_like(kc)
-    key = rng.integers(0, 65535, (T, Hkv, D), dtype=np.uint16)
-    val = rng.integers(0, 65535, (T, Hkv, D), dtype=np.uint16)
-    slots = rng.permutation(NB * B)[:T].astype(np.int64)
-
-    def one(i):
-        P.cache_write(kc, vc, key[i:i + 1], val[i:i + 1], slots[i:i + 1], B)
-
-    done, el = _timed_oracle(one, range(T), 8.0)
-    moved = 2 * 2 * done * Hkv * D * 2
-    return {"value": moved / el / 1e9, "unit": "GB/s (read+write)", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {T} tokens (K and V rows), numpy, 1 thread on {_cpu_name()}"}
 
 
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
@@ -414,23 +786,76 @@ def prefill_flops(context_lens, query_lens, num_heads, head_dim) -> int:
     return 4 * head_dim * num_heads * total
 
 
-def bench_prefill(args) -> dict:
-    """pa_prefill on LLaMA-7B-shaped prompts (32 heads of 128, fp16, blocks of
-    16): 8 sequences of 2048 tokens, either whole fresh prompts or the last
-    512 tokens after a 1536-token cached prefix (--prefix)."""
+def prefill_workload(prefix: int, fp8: bool):
+    """The prefill bench's inputs: 8 LLaMA-7B-shaped prompts of 2048 tokens
+    (32 heads of 128, fp16 queries, N(0,1)*0.5 values, blocks of 16, seed 7),
+    whose last 2048 - ``prefix`` tokens are the query rows; K/V pools in fp16
+    or as E4M3 codes with scale 0.5.  Returns (workload, query_start, q)."""
     import numpy as np
+
+    from workloads import build, normal_array
+    S, H, D, B, n = 8, 32, 128, 16, 2048
+    L = n - prefix
+    wl = build("llama7b_prefill_fp8kv" if fp8 else "llama7b_prefill_f16", "f16", [n] * S, H, H,
+               D, B, seed=7, pool="permutation", value_scale=0.5,
+               kv_dtype="fp8" if fp8 else None, kv_scale=0.5)
+    qs = np.arange(S + 1, dtype=np.int32) * L
+    q = normal_array(7, 40, (S * L, H, D), "f16", 0.5)
+    return wl, qs, q
+
+
+def _prefill_item(item):
+    import oracle.paged as P
+    st = _ORACLE_STATE
+    wl, qs, q = st["wl"], st["qs"], st["q"]
+    if wl.pool_dtype == "fp8":
+        P.paged_prefill_fp8(q, wl.key_cache, wl.value_cache, wl.block_tables,
+                            wl.context_lens, qs, wl.block_size, wl.scale, wl.dtype,
+                            wl.k_scale, wl.v_scale, wl.num_kv_heads, rows=[item])
+    else:
+        P.paged_prefill(q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens,
+                        qs, wl.block_size, wl.scale, wl.dtype, wl.num_kv_heads, rows=[item])
+    return 1
+
+
+def _prefill_cpu_baseline(wl, qs, q, prefix) -> dict:
+    """The float64 oracle's prefill on (row, head) pairs of the same workload
+    in a seeded random order (a representative mix of rows), on the host's
+    cores; reported as query tokens/s (a query token covers all heads)."""
+    import numpy as np
+
+    items = [(i, h) for i in range(int(qs[-1])) for h in range(wl.num_heads)]
+    order = np.random.default_rng(0).permutation(len(items))
+    items = [items[k] for k in order]
+    _ORACLE_STATE.update(wl=wl, qs=qs, q=q)
+    try:
+        run = parallel_oracle(_prefill_item, items, 12.0)
+    finally:
+        for k in ("wl", "qs", "q"):
+            _ORACLE_STATE.pop(k, None)
+    return _oracle_record(run["count"] / wl.num_heads / run["seconds"], "query tokens/s", run,
+                          f"{run['items']} of {len(items)} (query row, head) pairs in seeded "
+                          f"random order, {prefix}-token cached prefix, float64 numpy")
+
+
+def bench_prefill(args) -> dict:
+    """pa_prefill (pa_prefill_fp8 with --kv fp8) on LLaMA-7B-shaped prompts
+    (32 heads of 128, fp16, blocks of 16): 8 sequences of 2048 tokens, either
+    whole fresh prompts or the last 512 tokens after a 1536-token cached
+    prefix (--prefix)."""
+    fp8 = getattr(args, "kv", "f16") == "fp8"
+    wl, qs, q_raw = prefill_workload(args.prefix, fp8)
+    cpu = None if args.no_cpu_baseline else _prefill_cpu_baseline(wl, qs, q_raw, args.prefix)
+
     import torch
 
     import paged_kv_cache_368_amd as pa
-    from workloads import build, normal_array, to_torch
-
-    S, H, D, B, n = 8, 32, 128, 16, 2048
+    from workloads import to_torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    S, H, D, B = wl.num_seqs, wl.num_heads, wl.head_dim, wl.block_size
+    n = wl.max_context_len
     L = n - args.prefix
-    fp8 = getattr(args, "kv", "f16") == "fp8"
-    wl = build("llama7b_prefill_f16", "f16", [n] * S, H, H, D, B, seed=7, pool="permutation",
-               value_scale=0.5, kv_dtype="fp8" if fp8 else None, kv_scale=0.5)
-    qs = np.arange(S + 1, dtype=np.int32) * L
-    q = to_torch(normal_array(7, 40, (S * L, H, D), "f16", 0.5), "f16", "cuda")
+    q = to_torch(q_raw, "f16", "cuda")
     kc, vc = to_torch(wl.key_cache, wl.pool_dtype, "cuda"), to_torch(wl.value_cache, wl.pool_dtype, "cuda")
     bt = torch.tensor(wl.block_tables, device="cuda")
     cl = torch.tensor(wl.context_lens, device="cuda")
@@ -458,51 +883,23 @@ def bench_prefill(args) -> dict:
     wall = time.perf_counter() - t0
     mean = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e-3
     tflops = flops / mean / 1e12
+    entry = "pa_prefill_fp8" if fp8 else "pa_prefill"
     return {
-        "metric": "paged prefill (pa_prefill): query tokens/s and causal attention TFLOP/s",
+        "metric": f"paged prefill ({entry}): query tokens/s and causal attention TFLOP/s",
         "value": S * L / mean, "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16 (K/V fp8 e4m3)" if fp8 else "f16",
         "data": "synthetic (seeded N(0,1)*0.5 q/K/V, random block tables)",
-        "config": {"workload": "llama7b_prefill_f16", "num_seqs": S, "num_heads": H,
+        "config": {"workload": wl.name, "num_seqs": S, "num_heads": H,
                    "head_dim": D, "block_size": B, "context_len": n, "query_len": L,
                    "cached_prefix": args.prefix, "kv": "fp8 E4M3" if fp8 else "f16"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS["f16"],
                      "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS["f16"], "traffic": None,
                      "kernel": "prefill_kernel", "flops_per_launch": flops,
                      "mean_launch_us": mean * 1e6},
-        "cpu_baseline": None if args.no_cpu_baseline else _prefill_cpu_baseline(wl, qs, args.prefix),
+        "cpu_baseline": cpu,
     }
-
-
-def _prefill_cpu_baseline(wl, qs, prefix) -> dict:
-    """The float64 oracle's prefill on (row, head) pairs of the same workload
-    in order, single-threaded, for up to ~12 s; reported as query tokens/s
-    (a query token covers all heads)."""
-    import numpy as np
-
-    import oracle.paged as P
-    from workloads import normal_array
-
-    q = normal_array(7, 40, (int(qs[-1]), wl.num_heads, wl.head_dim), "f16", 0.5)
-    items = [(i, h) for i in range(int(qs[-1])) for h in range(wl.num_heads)]
-    order = np.random.default_rng(0).permutation(len(items))     # a representative mix of rows
-    items = [items[k] for k in order]
-
-    def one(item):
-        if wl.pool_dtype == "fp8":
-            P.paged_prefill_fp8(q, wl.key_cache, wl.value_cache, wl.block_tables,
-                                wl.context_lens, qs, wl.block_size, wl.scale, wl.dtype,
-                                wl.k_scale, wl.v_scale, wl.num_kv_heads, rows=[item])
-        else:
-            P.paged_prefill(q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens,
-                            qs, wl.block_size, wl.scale, wl.dtype, wl.num_kv_heads, rows=[item])
-
-    done, el = _timed_oracle(one, items, 12.0)
-    return {"value": done / wl.num_heads / el, "unit": "query tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} of {len(items)} (query row, head) pairs in seeded random order, "
-                      f"{prefix}-token cached prefix, float64 numpy, 1 thread on {_cpu_name()}"}
 
 
 def _bm_replay_lib(bm, events, max_blocks):
@@ -599,7 +996,8 @@ def bench_block_manager(args) -> dict:
 
 def _bm_cpu_baseline(setup, per_step, NB, B, max_blocks) -> dict:
     """The oracle's block manager (plain Python) on the same schedule from its
-    start, until ~10 s are spent."""
+    start, until ~10 s are spent.  One manager is one sequence of state
+    changes, so this runs on one core (as does the library's manager)."""
     import oracle.blocks as OB
     om = OB.BlockManager(NB, B)
     for ev in setup:
@@ -615,7 +1013,8 @@ def _bm_cpu_baseline(setup, per_step, NB, B, max_blocks) -> dict:
     el = time.perf_counter() - t0
     return {"value": appends / el, "unit": "appended tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the first {steps_done} decode steps of the same schedule (after its "
-                      f"setup), plain Python, 1 thread on {_cpu_name()}"}
+                      f"setup), plain Python, 1 thread (one manager's state changes are "
+                      f"sequential) on {_cpu_name()}"}
 
 
 def main(argv=None) -> int:
@@ -623,9 +1022,12 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1,
-                    help="workload index 0..6 (default 1: LLaMA-7B shape; 5 and 6: the LLaMA-7B "
-                         "and 70B-style GQA shapes with fp8 K/V)")
+    ap.add_argument("--config", type=int, default=None,
+                    help="time only this workload (0..6) as the line; default: the long-context "
+                         f"workload {HEADLINE_CONFIG} as the line, the others as sub_records")
+    ap.add_argument("--sub-configs", default=None,
+                    help=f"workloads timed as sub_records, e.g. '{SUB_CONFIGS}' (index[:block "
+                         "size]); default: those when --config is not given, else none")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--seed", type=int, default=None)
@@ -654,227 +1056,9 @@ def main(argv=None) -> int:
               "(run with --gpus 1)", file=sys.stderr)
         return 2
 
-    if args.op == "block_manager":                   # host only
-        print(json.dumps(bench_block_manager(args)), flush=True)
-        return 0
-
-    import torch
-
-    import paged_kv_cache_368_amd as pa
-    from workloads import make_workload, to_device, to_torch
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    pa.load_library()
-    if args.op == "copy_blocks":
-        print(json.dumps(bench_copy_blocks(args)), flush=True)
-        return 0
-    if args.op == "prefill":
-        print(json.dumps(bench_prefill(args)), flush=True)
-        return 0
-    if args.op == "cache_write":
-        print(json.dumps(bench_cache_write(args)), flush=True)
-        return 0
-    dev_name = torch.cuda.get_device_name(0)
-    print(f"[bench] device {dev_name}; building workload {args.config}", file=sys.stderr, flush=True)
-    wl = make_workload(args.config, seed=args.seed, block_size=args.block_size)
-    if args.partition_size is not None:
-        wl.partition_size = args.partition_size
-    S, H, Hkv, D, B = wl.num_seqs, wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
-    dt = wl.dtype
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
-    maxctx = wl.max_context_len
-    fp8 = wl.pool_dtype == "fp8"
-    size_dt = pa.PA_FP8_E4M3 if fp8 else pa.DTYPE_CODES[tdt]
-    lib = pa.load_library()
-    P_used = lib.pa_decode_partition_size(S, H, Hkv, D, B, maxctx, wl.partition_size, size_dt)
-    ws_bytes = lib.pa_decode_workspace_size(S, H, Hkv, D, B, maxctx, wl.partition_size, size_dt)
-    fused = args.step == "fused"
-    nbytes = algorithmic_bytes(wl.context_lens, H, Hkv, D, B, dt, wl.pool_dtype,
-                               new_row_write=fused)
-    sum_ctx = int(wl.context_lens.sum())
-
-    base = to_device(wl)
-    pool_bytes = base.key_cache.numel() * base.key_cache.element_size() * 2
-    copies = max(2, math.ceil(2 * MALL_BYTES / pool_bytes) + 1)
-    pools = [(base.key_cache, base.value_cache)] + [
-        (base.key_cache.clone(), base.value_cache.clone()) for _ in range(copies - 1)]
-    slots = torch.empty(S, dtype=torch.int64, device="cuda")
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-    print(f"[bench] {wl.name}: S={S} H={H}/{Hkv} D={D} B={B} {dt} sum(ctx)={sum_ctx} "
-          f"P={P_used} pool copies={copies} ({pool_bytes / 2**20:.0f} MiB each)",
-          file=sys.stderr, flush=True)
-
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        kc, vc = pools[i % copies]
-        if fused:
-            if ev is not None:
-                ev[0].record(stream)
-            if fp8:
-                pa.pa_append_decode_fp8(base.out, base.q, base.new_key, base.new_value, kc, vc,
-                                        base.block_tables, base.context_lens, maxctx,
-                                        wl.k_scale, wl.v_scale, wl.scale, wl.partition_size,
-                                        workspace)
-            else:
-                pa.pa_append_decode(base.out, base.q, base.new_key, base.new_value, kc, vc,
-                                    base.block_tables, base.context_lens, maxctx, wl.scale,
-                                    wl.partition_size, workspace)
-            if ev is not None:
-                ev[1].record(stream)
-            return
-        pa.pa_compute_slots(slots, base.block_tables, B, wl.num_blocks, context_lens=base.context_lens)
-        if fp8:
-            pa.pa_cache_write_fp8(base.new_key, base.new_value, kc, vc, slots, wl.k_scale,
-                                  wl.v_scale)
-        else:
-            pa.pa_cache_write(base.new_key, base.new_value, kc, vc, slots)
-        if ev is not None:
-            ev[0].record(stream)
-        if fp8:
-            pa.pa_decode_fp8(base.out, base.q, kc, vc, base.block_tables, base.context_lens,
-                             maxctx, wl.k_scale, wl.v_scale, wl.scale, wl.partition_size,
-                             workspace)
-        else:
-            pa.pa_decode(base.out, base.q, kc, vc, base.block_tables, base.context_lens, maxctx,
-                         wl.scale, wl.partition_size, workspace)
-        if ev is not None:
-            ev[1].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Launch durations from HIP events on the kernels' stream.  One-launch
-    # steps: an event pair brackets each run of EVENT_EVERY consecutive steps
-    # (launch duration = elapsed / run length), so the events' own cost (~8 us
-    # per pair on a ~105 us LLaMA-7B step) is paid once per run.  Three-call
-    # steps: the pair brackets the decode call of every EVENT_EVERY-th step.
-    # Fewer than 2 * EVENT_EVERY timed steps: every step is measured alone.
-    every = EVENT_EVERY if args.steps >= 2 * EVENT_EVERY else 1
-    samples = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if fused:
-        for g0 in range(0, args.steps, every):
-            g1 = min(g0 + every, args.steps)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(g0, g1):
-                step(args.warmup + i)
-            e1.record(stream)
-            samples.append((e0, e1, g1 - g0))
-    else:
-        for i in range(args.steps):
-            if i % every == 0:
-                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                samples.append((ev[0], ev[1], 1))
-                step(args.warmup + i, ev)
-            else:
-                step(args.warmup + i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dec_ms = sorted(e0.elapsed_time(e1) / n for e0, e1, n in samples)
-    dec_mean_s = sum(dec_ms) / len(dec_ms) / 1e3
-    dec_med_s = dec_ms[len(dec_ms) // 2] / 1e3
-    print(f"[bench] {args.steps} steps in {wall * 1e3:.2f} ms; decode mean {dec_mean_s * 1e6:.1f} us "
-          f"median {dec_med_s * 1e6:.1f} us p10 {dec_ms[len(dec_ms) // 10] * 1e3:.1f} us "
-          f"p90 {dec_ms[(9 * len(dec_ms)) // 10] * 1e3:.1f} us", file=sys.stderr, flush=True)
-
-    ceiling = None
-    if not args.no_ceiling:
-        # The achievable read rate on this machine (pa_read_probe over 2 GiB):
-        # in index order, and as 4 KB tiles in random order, the decode
-        # kernels' pattern (one (block, kv head) tile of K or V at a time).
-        big = torch.ones(1 << 29, dtype=torch.int32, device="cuda")
-        sink = torch.empty(pa.PA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
-        perm = torch.randperm(big.numel() * 4 // 4096, device="cuda",
-                              generator=torch.Generator(device="cuda").manual_seed(0)).int()
-        # Also the call's own pattern at its own size: its (block, kv head)
-        # tiles (B x D x element bytes) in random order over as many bytes as
-        # its K and V (a shorter read pays its ramp-up and tail on fewer
-        # bytes; fp8 tiles are half the size).
-        tile = max(1024, B * D * ELEM[wl.pool_dtype or dt])
-        n_same = max(1, min(nbytes["kv"] // tile, big.numel() * 4 // tile))
-        perm_same = torch.randperm(n_same, device="cuda",
-                                   generator=torch.Generator(device="cuda").manual_seed(1)).int()
-        ceiling = {"how": "pa_read_probe, best of 5 HIP-event-timed calls: 2 GiB in index "
-                          "order, 2 GiB as random 4 KB tiles, the call's K+V bytes as its own "
-                          "tiles in random order",
-                   "same_bytes_tile_bytes": tile}
-        for key, buf, tb, order in (("contiguous_gbps", big, 4096, None),
-                                    ("random_4k_tiles_gbps", big, 4096, perm),
-                                    ("random_tiles_same_bytes_gbps",
-                                     big[:n_same * tile // 4], tile, perm_same)):
-            pa.pa_read_probe(buf, tb, order, sink)
-            best = float("inf")
-            for _ in range(5):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                pa.pa_read_probe(buf, tb, order, sink)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                best = min(best, e0.elapsed_time(e1) / 1e3)
-            ceiling[key] = buf.numel() * 4 / best / 1e9
-        del big, perm, perm_same, sink
-        torch.cuda.synchronize()
-
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    achieved = nbytes["total"] / dec_mean_s / 1e9
-    result = {
-        "metric": METRIC,
-        "value": sum_ctx * args.steps / wall,
-        "unit": "context tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": wall * 1e3 / args.steps,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dt if not fp8 else f"{dt} (K/V fp8 e4m3)",
-        "data": "synthetic (seeded N(0,1) K/V/q, random block tables; no dataset)",
-        "config": {"workload": wl.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
-                   "head_dim": D, "block_size": B, "sum_context_tokens": sum_ctx,
-                   "max_context_len": maxctx, "partition_size": P_used, "seed": wl.seed,
-                   "pool_copies_rotated": copies,
-                   "step": ("pa_append_decode(_fp8): slot, K/V write and attention in one "
-                            "launch" if fused else "pa_compute_slots + pa_cache_write(_fp8) + "
-                            "pa_decode(_fp8)")},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(wl.name, B, P_used, fused),
-                     "kernel": ("pa_append_decode" if fused else "pa_decode") +
-                               ("_fp8" if fp8 else "") +
-                               " (decode kernel + merge pass when split)",
-                     "bytes_per_launch": nbytes["total"], "mean_launch_us": dec_mean_s * 1e6,
-                     "median_launch_us": dec_med_s * 1e6, "event_samples": len(dec_ms),
-                     "launches_per_sample": every if fused else 1,
-                     "p10_launch_us": dec_ms[len(dec_ms) // 10] * 1e3,
-                     "p90_launch_us": dec_ms[(9 * len(dec_ms)) // 10] * 1e3},
-        "read_ceiling": ceiling,
-        "frac_of_tile_ceiling": (achieved / ceiling["random_4k_tiles_gbps"]) if ceiling else None,
-        "frac_of_same_bytes_tile_ceiling":
-            (achieved / ceiling["random_tiles_same_bytes_gbps"]) if ceiling else None,
-        "decode_context_tokens_per_s": sum_ctx / dec_mean_s,
-        "device": dev_name,
-    }
-    if not args.no_cpu_baseline:
-        print("[bench] timing the float64 oracle on a host sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl)
-    else:
-        result["cpu_baseline"] = None
-    print(json.dumps(result), flush=True)
+    run = {"decode": bench_decode, "copy_blocks": bench_copy_blocks, "prefill": bench_prefill,
+           "cache_write": bench_cache_write, "block_manager": bench_block_manager}[args.op]
+    print(json.dumps(run(args)), flush=True)
     return 0
 
 

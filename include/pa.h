@@ -159,7 +159,11 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
  *   partition_size      tokens per split-context partition, 0 = choose;
  *                       must be a multiple of block_size and of 16
  *   workspace           device memory of >= pa_decode_workspace_size(...)
- *                       bytes, or NULL when that size is 0
+ *                       bytes, 256-byte aligned, or NULL when that size is
+ *                       0; the caller's, its contents on entry do not
+ *                       matter.  Memory the GPU cannot reach (pageable host
+ *                       memory) is refused with PA_ERR_INVALID_ARGUMENT;
+ *                       pinned host memory is accepted.
  *
  * A sequence with context_lens[s] == 0 gets zeros.  A sequence whose
  * context_lens value is negative or above max_context_len or

@@ -9,6 +9,7 @@ from ._capi import (  # noqa: F401
     LIB_PATH,
     PaError,
     declared_functions,
+    decode_workspace,
     load_library,
     PA_FP8_E4M3,
     PA_READ_PROBE_SINK_WORDS,

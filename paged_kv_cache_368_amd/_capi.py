@@ -9,7 +9,6 @@ one libpa.so binds to (both carry the soname libamdhip64.so.7).
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 import re
 
@@ -144,6 +143,28 @@ def _opt(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _workspace(workspace):
+    """(pointer, bytes) of the caller's decode workspace, or (None, 0).  The
+    library checks the size and refuses a split-context call without one."""
+    if workspace is None:
+        return None, 0
+    _dev(workspace, "workspace")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def decode_workspace(q: torch.Tensor, key_cache: torch.Tensor, max_context_len: int,
+                     partition_size: int = 0) -> torch.Tensor | None:
+    """Allocate the device workspace that pa_decode / pa_append_decode (or
+    their _fp8 forms, for uint8 pools) need for these inputs, or return None
+    when they need none.  The decode calls themselves never allocate: a caller
+    allocates this once and passes it to every call of that size or smaller."""
+    S, H, D = q.shape
+    _, Hkv, B, _ = key_cache.shape
+    dt = torch.uint8 if key_cache.dtype == torch.uint8 else q.dtype
+    n = pa_decode_workspace_size(S, H, Hkv, D, B, max_context_len, partition_size, dt)
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
 def pa_version() -> str:
     return load_library().pa_version().decode()
 
@@ -263,7 +284,7 @@ def pa_cache_write_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.
 def pa_decode_fp8(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
                   value_cache: torch.Tensor, block_tables: torch.Tensor,
                   context_lens: torch.Tensor, max_context_len: int, k_scale: float,
-                  v_scale: float, scale: float | None = None, partition_size: int = 0,
+                  v_scale: float, scale: float, partition_size: int = 0,
                   workspace: torch.Tensor | None = None) -> torch.Tensor:
     """PagedAttention decode over uint8 E4M3 pools (values code * scale) into
     ``out`` [S][H][D] of q's type (fp16/bf16); see include/pa.h."""
@@ -283,15 +304,7 @@ def pa_decode_fp8(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
         raise ValueError("shape mismatch between q, out and the pools")
     if block_tables.shape[0] != S or context_lens.numel() != S:
         raise ValueError("block_tables and context_lens must have one row per sequence")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    n = lib.pa_decode_workspace_size(S, H, Hkv, D, B, max_context_len, partition_size, PA_FP8_E4M3)
-    if n == ctypes.c_size_t(-1).value:
-        raise PaError(PA_ERR_INVALID_ARGUMENT, pa_last_error())
-    if n and workspace is None:
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(lib.pa_decode_fp8(
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
         ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
@@ -304,7 +317,7 @@ def pa_decode_fp8(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
 def pa_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
                value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                query_start: torch.Tensor, max_query_len: int, max_context_len: int,
-               scale: float | None = None) -> torch.Tensor:
+               scale: float) -> torch.Tensor:
     """Paged prefill into ``out`` [T][H][D] for query rows ``q`` [T][H][D]
     (fp16/bf16); sequence s owns rows query_start[s] .. query_start[s+1]-1,
     the last tokens of its context; see include/pa.h."""
@@ -327,8 +340,6 @@ def pa_prefill(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
         raise ValueError("shape mismatch between q, out and the pools")
     if block_tables.shape[0] != S or query_start.numel() != S + 1:
         raise ValueError("block_tables needs one row and query_start S + 1 entries")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     _check(lib.pa_prefill(
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
         ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
@@ -342,7 +353,7 @@ def pa_prefill_fp8(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
                    value_cache: torch.Tensor, block_tables: torch.Tensor,
                    context_lens: torch.Tensor, query_start: torch.Tensor, max_query_len: int,
                    max_context_len: int, k_scale: float, v_scale: float,
-                   scale: float | None = None) -> torch.Tensor:
+                   scale: float) -> torch.Tensor:
     """pa_prefill over uint8 E4M3 pools (values code * scale): query rows
     ``q`` [T][H][D] (fp16/bf16) into ``out``; see include/pa.h."""
     lib = load_library()
@@ -365,8 +376,6 @@ def pa_prefill_fp8(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
         raise ValueError("shape mismatch between q, out and the pools")
     if block_tables.shape[0] != S or query_start.numel() != S + 1:
         raise ValueError("block_tables needs one row and query_start S + 1 entries")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     _check(lib.pa_prefill_fp8(
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
         ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
@@ -381,13 +390,13 @@ def pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, block_
                              max_context_len, partition_size=0, dtype=torch.float16) -> int:
     return load_library().pa_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim,
                                                    block_size, max_context_len, partition_size,
-                                                   DTYPE_CODES[dtype])
+                                                   _size_dtype(dtype))
 
 
 def pa_append_decode(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                      key_cache: torch.Tensor, value_cache: torch.Tensor,
                      block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
-                     scale: float | None = None, partition_size: int = 0,
+                     scale: float, partition_size: int = 0,
                      workspace: torch.Tensor | None = None) -> torch.Tensor:
     """One decode step in one launch: writes each sequence's newest token
     (position context_lens - 1; rows ``key``/``value`` [S][Hkv][D]) into its
@@ -411,13 +420,7 @@ def pa_append_decode(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor, valu
         raise ValueError("key and value must be [num_seqs][num_kv_heads][head_dim]")
     if block_tables.shape[0] != S or context_lens.numel() != S:
         raise ValueError("block_tables and context_lens must have one row per sequence")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    need = pa_decode_workspace_size(S, H, Hkv, D, B, max_context_len, partition_size, q.dtype)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(lib.pa_append_decode(
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
         ctypes.c_void_p(key.data_ptr()), ctypes.c_void_p(value.data_ptr()),
@@ -432,7 +435,7 @@ def pa_append_decode_fp8(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor,
                          value: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                          block_tables: torch.Tensor, context_lens: torch.Tensor,
                          max_context_len: int, k_scale: float, v_scale: float,
-                         scale: float | None = None, partition_size: int = 0,
+                         scale: float, partition_size: int = 0,
                          workspace: torch.Tensor | None = None) -> torch.Tensor:
     """pa_append_decode over E4M3 pools (uint8 codes, value = code * scale):
     the newest token's rows (``key``/``value`` [S][Hkv][D], q's type) are
@@ -457,15 +460,7 @@ def pa_append_decode_fp8(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor,
         raise ValueError("key and value must be [num_seqs][num_kv_heads][head_dim]")
     if block_tables.shape[0] != S or context_lens.numel() != S:
         raise ValueError("block_tables and context_lens must have one row per sequence")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    n = lib.pa_decode_workspace_size(S, H, Hkv, D, B, max_context_len, partition_size, PA_FP8_E4M3)
-    if n == ctypes.c_size_t(-1).value:
-        raise PaError(PA_ERR_INVALID_ARGUMENT, pa_last_error())
-    if n and workspace is None:
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(lib.pa_append_decode_fp8(
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
         ctypes.c_void_p(key.data_ptr()), ctypes.c_void_p(value.data_ptr()),
@@ -480,8 +475,8 @@ def pa_append_decode_fp8(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor,
 PA_READ_PROBE_SINK_WORDS = 2048
 
 
-def pa_read_probe(buf: torch.Tensor, tile_bytes: int, order: torch.Tensor | None = None,
-                  sink: torch.Tensor | None = None) -> torch.Tensor:
+def pa_read_probe(buf: torch.Tensor, tile_bytes: int, order: torch.Tensor | None,
+                  sink: torch.Tensor) -> torch.Tensor:
     """Read ``buf`` as tiles of ``tile_bytes`` in ``order`` (int32 tile
     indices; None: index order) with the library's read probe; returns the
     sink (one uint32 fold per work-group).  The caller times the call."""
@@ -495,19 +490,28 @@ def pa_read_probe(buf: torch.Tensor, tile_bytes: int, order: torch.Tensor | None
         _dev(order, "order")
         if order.dtype != torch.int32 or order.numel() != n:
             raise ValueError("order must be int32 with one entry per tile")
-    if sink is None:
-        sink = torch.empty(PA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    _dev(sink, "sink")
+    if sink.numel() * sink.element_size() < PA_READ_PROBE_SINK_WORDS * 4:
+        raise ValueError(f"sink must hold {PA_READ_PROBE_SINK_WORDS} 32-bit words")
     _check(lib.pa_read_probe(ctypes.c_void_p(buf.data_ptr()), tile_bytes, n,
                              ctypes.c_void_p(order.data_ptr()) if order is not None else None,
                              ctypes.c_void_p(sink.data_ptr()), _stream(buf)))
     return sink
 
 
+def _size_dtype(dtype) -> int:
+    """dtype code of the sizing functions: a torch float type, or torch.uint8
+    (or PA_FP8_E4M3) for E4M3 pools."""
+    if dtype == torch.uint8 or dtype == PA_FP8_E4M3:
+        return PA_FP8_E4M3
+    return DTYPE_CODES[dtype]
+
+
 def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                              max_context_len, partition_size=0, dtype=torch.float16) -> int:
     n = load_library().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
                                                 block_size, max_context_len, partition_size,
-                                                DTYPE_CODES[dtype])
+                                                _size_dtype(dtype))
     if n == ctypes.c_size_t(-1).value:
         raise PaError(PA_ERR_INVALID_ARGUMENT, pa_last_error())
     return n
@@ -515,12 +519,12 @@ def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_
 
 def pa_decode(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
               value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
-              max_context_len: int, scale: float | None = None, partition_size: int = 0,
+              max_context_len: int, scale: float, partition_size: int = 0,
               workspace: torch.Tensor | None = None) -> torch.Tensor:
     """PagedAttention decode into ``out`` [S][H][D]; see include/pa.h.
 
-    ``workspace`` (uint8, >= pa_decode_workspace_size bytes) may be passed to
-    keep the call free of allocation; otherwise one is allocated here.
+    ``workspace``: uint8 device memory of >= pa_decode_workspace_size bytes
+    (``decode_workspace`` allocates one), or None when that size is 0.
     """
     lib = load_library()
     for n, t in (("out", out), ("q", q), ("key_cache", key_cache), ("value_cache", value_cache),
@@ -536,14 +540,8 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
         raise ValueError("shape mismatch between q, out and the pools")
     if block_tables.shape[0] != S or context_lens.numel() != S:
         raise ValueError("block_tables and context_lens must have one row per sequence")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     dt = DTYPE_CODES[q.dtype]
-    need = pa_decode_workspace_size(S, H, Hkv, D, B, max_context_len, partition_size, q.dtype)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(lib.pa_decode(
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
         ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),

@@ -283,6 +283,12 @@ pa_status_t decode_impl(void *out, const void *q, const void *key_cache, const v
                       std::to_string(z.ws_bytes) + " bytes");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(PA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    // The kernels write the partials there: refuse memory the GPU cannot
+    // reach (pageable host memory) instead of handing it to them.
+    workspace = const_cast<void *>(device_view(workspace));
+    if (!workspace)
+      return fail(PA_ERR_INVALID_ARGUMENT,
+                  "workspace must be device memory or pinned (hipHostMalloc) host memory");
   }
 
   pa::DecodeArgs a;

@@ -264,3 +264,15 @@ def test_read_probe_rejects(lib):
     assert rp(_p(), 4096, 8, None, None, None) == _capi.PA_ERR_INVALID_ARGUMENT
     assert rp(_p(8), 4096, 8, None, _p(), None) == _capi.PA_ERR_INVALID_ARGUMENT
     assert rp(None, 4096, 0, None, None, None) == _capi.PA_OK
+
+
+def test_decode_refuses_a_workspace_the_gpu_cannot_reach(lib):
+    """A split-context call writes its partials into the workspace: pageable
+    host memory is refused with PA_ERR_INVALID_ARGUMENT before any launch."""
+    need = lib.pa_decode_workspace_size(2, 8, 8, 128, 16, 128, 16, F16)
+    assert 0 < need < 1 << 20
+    host = ctypes.create_string_buffer(need + 256)
+    addr = (ctypes.addressof(host) + 255) & ~255            # aligned, large enough, host memory
+    st = _decode(lib, P=16, maxctx=128, ws=ctypes.c_void_p(addr), wsb=need)
+    assert st == _capi.PA_ERR_INVALID_ARGUMENT
+    assert "workspace" in pa.pa_last_error()

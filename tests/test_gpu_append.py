@@ -58,7 +58,8 @@ def _append(wl, ps=0, dev=None):
     dev = dev or to_device(wl)
     pa.pa_append_decode(dev.out, dev.q, dev.new_key, dev.new_value, dev.key_cache,
                         dev.value_cache, dev.block_tables, dev.context_lens, wl.max_context_len,
-                        wl.scale, ps)
+                        wl.scale, ps,
+                        workspace=pa.decode_workspace(dev.q, dev.key_cache, wl.max_context_len, ps))
     torch.cuda.synchronize()
     return dev
 
@@ -107,7 +108,8 @@ def test_append_decode_matches_step_of_three_calls(dtype, D, H, Hkv):
                         context_lens=b.context_lens)
     pa.pa_cache_write(b.new_key, b.new_value, b.key_cache, b.value_cache, slots)
     pa.pa_decode(b.out, b.q, b.key_cache, b.value_cache, b.block_tables, b.context_lens,
-                 wl.max_context_len, wl.scale, 256)
+                 wl.max_context_len, wl.scale, 256,
+                 workspace=pa.decode_workspace(b.q, b.key_cache, wl.max_context_len, 256))
     torch.cuda.synchronize()
     assert torch.equal(a.key_cache.view(torch.int16), b.key_cache.view(torch.int16))
     assert torch.equal(a.value_cache.view(torch.int16), b.value_cache.view(torch.int16))
@@ -146,7 +148,8 @@ def test_append_decode_steps_in_a_row():
         dev.context_lens.copy_(torch.tensor(ctx, dtype=torch.int32))
         pa.pa_append_decode(dev.out, dev.q, dev.new_key, dev.new_value, dev.key_cache,
                             dev.value_cache, dev.block_tables, dev.context_lens,
-                            int(ctx.max()), wl.scale, 0)
+                            int(ctx.max()), wl.scale, 0,
+                            workspace=pa.decode_workspace(dev.q, dev.key_cache, int(ctx.max()), 0))
         torch.cuda.synchronize()
         slots = P.compute_slots(tables, B, wl.num_blocks, context_lens=ctx)
         P.cache_write(kc, vc, wl.new_key, wl.new_value, slots, B)
@@ -176,7 +179,8 @@ def test_append_decode_invalid_values():
     dev = to_device(wl)
     for ps in (0, 16):
         pa.pa_append_decode(dev.out, dev.q, dev.new_key, dev.new_value, dev.key_cache,
-                            dev.value_cache, dev.block_tables, dev.context_lens, 80, wl.scale, ps)
+                            dev.value_cache, dev.block_tables, dev.context_lens, 80, wl.scale, ps,
+                            workspace=pa.decode_workspace(dev.q, dev.key_cache, 80, ps))
         torch.cuda.synchronize()
         got = P.to_f64(from_torch(dev.out, "f16"), "f16")
         assert np.isnan(got[1:]).all(), f"P={ps}: rows not poisoned"
@@ -196,7 +200,8 @@ def test_append_decode_full_size_sampled(idx):
     dev = to_device(wl)
     pa.pa_append_decode(dev.out, dev.q, dev.new_key, dev.new_value, dev.key_cache,
                         dev.value_cache, dev.block_tables, dev.context_lens, wl.max_context_len,
-                        wl.scale, wl.partition_size)
+                        wl.scale, wl.partition_size,
+                        workspace=pa.decode_workspace(dev.q, dev.key_cache, wl.max_context_len, wl.partition_size))
     torch.cuda.synchronize()
     rng = np.random.default_rng(1)
     pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, wl.num_seqs, 24),

@@ -86,7 +86,8 @@ def test_swap_out_and_in_through_pinned_host_keeps_decode():
     out = torch.empty_like(dq)
     bt = torch.tensor([table], dtype=torch.int32, device="cuda")
     cl = torch.tensor([n], dtype=torch.int32, device="cuda")
-    pa.pa_decode(out, dq, dk, dv, bt, cl, n)
+    pa.pa_decode(out, dq, dk, dv, bt, cl, n, 1.0 / np.sqrt(D),
+                 workspace=pa.decode_workspace(dq, dk, n, 0))
     before = from_torch(out, dtype).copy()
 
     hk = torch.empty((12, Hkv, B, D), dtype=torch.float16, pin_memory=True).fill_(7.0)
@@ -106,7 +107,8 @@ def test_swap_out_and_in_through_pinned_host_keeps_decode():
     in_pairs = [(i, b) for i, b in enumerate(new_table[:nblk])]
     pa.pa_copy_blocks(dk, hk, _pairs_dev(in_pairs), dv, hv)
     bt2 = torch.tensor([new_table], dtype=torch.int32, device="cuda")
-    pa.pa_decode(out, dq, dk, dv, bt2, cl, n)
+    pa.pa_decode(out, dq, dk, dv, bt2, cl, n, 1.0 / np.sqrt(D),
+                 workspace=pa.decode_workspace(dq, dk, n, 0))
     torch.cuda.synchronize()
     assert from_torch(out, dtype).tobytes() == before.tobytes()
 
@@ -189,9 +191,11 @@ def test_decode_session_with_block_manager():
         ctx = np.array([lens[r] for r in rids], np.int32)
         q = _pool(seed, 500 + step, (len(rids), H, D), dtype)
         out = torch.empty((len(rids), H, D), dtype=tdt, device="cuda")
-        pa.pa_decode(out, to_torch(q, dtype, "cuda"), dk, dv,
+        dq = to_torch(q, dtype, "cuda")
+        pa.pa_decode(out, dq, dk, dv,
                      torch.tensor(tables, device="cuda"), torch.tensor(ctx, device="cuda"),
-                     int(ctx.max()))
+                     int(ctx.max()), 1.0 / np.sqrt(D),
+                     workspace=pa.decode_workspace(dq, dk, int(ctx.max())))
         torch.cuda.synchronize()
         assert from_torch(dk, dtype).tobytes() == kc.tobytes()
         assert from_torch(dv, dtype).tobytes() == vc.tobytes()

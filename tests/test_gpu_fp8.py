@@ -31,7 +31,8 @@ def _fp8_decode(wl, dev=None, partition_size=0):
     dev = dev or to_device(wl)
     pa.pa_decode_fp8(dev.out, dev.q, dev.key_cache, dev.value_cache, dev.block_tables,
                      dev.context_lens, wl.max_context_len, wl.k_scale, wl.v_scale, wl.scale,
-                     partition_size)
+                     partition_size,
+                     workspace=pa.decode_workspace(dev.q, dev.key_cache, wl.max_context_len, partition_size))
     torch.cuda.synchronize()
     return P.to_f64(from_torch(dev.out, wl.dtype), wl.dtype)
 
@@ -176,7 +177,8 @@ def test_append_decode_fp8_matches_oracle(name, kw, qt):
         dev = to_device(wl)
         pa.pa_append_decode_fp8(dev.out, dev.q, dev.new_key, dev.new_value, dev.key_cache,
                                 dev.value_cache, dev.block_tables, dev.context_lens,
-                                wl.max_context_len, wl.k_scale, wl.v_scale, wl.scale, ps)
+                                wl.max_context_len, wl.k_scale, wl.v_scale, wl.scale, ps,
+                                workspace=pa.decode_workspace(dev.q, dev.key_cache, wl.max_context_len, ps))
         torch.cuda.synchronize()
         got = P.to_f64(from_torch(dev.out, qt), qt)
         BD.assert_close(got, ref, qt, f"{name} P={ps}")

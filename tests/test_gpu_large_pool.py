@@ -140,7 +140,8 @@ def test_decode_on_pool_beyond_4gib(dtype, H, Hkv, D, B, ps):
     q = to_torch(q_raw, dtype, "cuda")
     out = torch.empty_like(q)
     scale = 1.0 / math.sqrt(D)
-    pa.pa_decode(out, q, bp.k_dev, bp.v_dev, bp.tables_dev, bp.ctx_dev, bp.max_ctx(), scale, ps)
+    pa.pa_decode(out, q, bp.k_dev, bp.v_dev, bp.tables_dev, bp.ctx_dev, bp.max_ctx(), scale, ps,
+                 workspace=pa.decode_workspace(q, bp.k_dev, bp.max_ctx(), ps))
     torch.cuda.synchronize()
     ref = P.paged_decode(q_raw, bp.kc, bp.vc, bp.ctables, bp.ctx, B, scale, dtype, Hkv)
     got = P.to_f64(from_torch(out, dtype), dtype)
@@ -186,7 +187,8 @@ def test_slots_write_and_append_on_pool_beyond_4gib(dtype, H, Hkv):
     out = torch.empty_like(q)
     pa.pa_append_decode(out, q, to_torch(nk, dtype, "cuda"), to_torch(nv, dtype, "cuda"),
                         bp.k_dev, bp.v_dev, bp.tables_dev, bp.ctx_dev, bp.max_ctx(),
-                        1.0 / math.sqrt(D), 0)
+                        1.0 / math.sqrt(D), 0,
+                        workspace=pa.decode_workspace(q, bp.k_dev, bp.max_ctx(), 0))
     torch.cuda.synchronize()
     new_slots = P.compute_slots(bp.ctables, B, len(bp.ids), context_lens=ctx1)
     P.cache_write(bp.kc, bp.vc, nk, nv, new_slots, B)
@@ -227,7 +229,8 @@ def test_fp8_write_and_decode_on_pool_beyond_4gib(qt, H, Hkv):
     for ps in (0, 512):
         out = torch.empty_like(q)
         pa.pa_decode_fp8(out, q, bp.k_dev, bp.v_dev, bp.tables_dev, bp.ctx_dev, bp.max_ctx(),
-                         ks, vs, scale, ps)
+                         ks, vs, scale, ps,
+                         workspace=pa.decode_workspace(q, bp.k_dev, bp.max_ctx(), ps))
         torch.cuda.synchronize()
         ref = P.paged_decode_fp8(q_raw, bp.kc, bp.vc, bp.ctables, bp.ctx, B, scale, qt, ks, vs, Hkv)
         BD.assert_close(P.to_f64(from_torch(out, qt), qt), ref, qt, f"fp8 decode P={ps}")
@@ -236,7 +239,8 @@ def test_fp8_write_and_decode_on_pool_beyond_4gib(qt, H, Hkv):
     nv = normal_array(923, 7, (S, Hkv, D), qt)
     out = torch.empty_like(q)
     pa.pa_append_decode_fp8(out, q, to_torch(nk, qt, "cuda"), to_torch(nv, qt, "cuda"), bp.k_dev,
-                            bp.v_dev, bp.tables_dev, bp.ctx_dev, bp.max_ctx(), ks, vs, scale, 0)
+                            bp.v_dev, bp.tables_dev, bp.ctx_dev, bp.max_ctx(), ks, vs, scale, 0,
+                            workspace=pa.decode_workspace(q, bp.k_dev, bp.max_ctx(), 0))
     torch.cuda.synchronize()
     new_slots = P.compute_slots(bp.ctables, B, len(bp.ids), context_lens=bp.ctx)
     P.cache_write_fp8(bp.kc, bp.vc, nk, nv, new_slots, B, qt, ks, vs)

@@ -38,7 +38,8 @@ def _run_decode(wl, partition_size=None, dev=None):
     dev = dev or to_device(wl)
     ps = wl.partition_size if partition_size is None else partition_size
     pa.pa_decode(dev.out, dev.q, dev.key_cache, dev.value_cache, dev.block_tables,
-                 dev.context_lens, wl.max_context_len, wl.scale, ps)
+                 dev.context_lens, wl.max_context_len, wl.scale, ps,
+                 workspace=pa.decode_workspace(dev.q, dev.key_cache, wl.max_context_len, ps))
     torch.cuda.synchronize()
     return P.to_f64(from_torch(dev.out, wl.dtype), wl.dtype)
 
@@ -236,7 +237,8 @@ def test_decode_invalid_device_values_poison_only_their_row():
     dev = to_device(wl)
     for ps in (0, 16):
         pa.pa_decode(dev.out, dev.q, dev.key_cache, dev.value_cache, dev.block_tables,
-                     dev.context_lens, 80, wl.scale, ps)
+                     dev.context_lens, 80, wl.scale, ps,
+                     workspace=pa.decode_workspace(dev.q, dev.key_cache, 80, ps))
         torch.cuda.synchronize()
         got = P.to_f64(from_torch(dev.out, "f16"), "f16")
         assert np.isnan(got[1]).all(), f"P={ps}: bad block id row not poisoned: {got[1, :, :4]}"
@@ -255,7 +257,8 @@ def test_decode_step_slots_write_attend():
                         context_lens=dev.context_lens)
     pa.pa_cache_write(dev.new_key, dev.new_value, dev.key_cache, dev.value_cache, slots)
     pa.pa_decode(dev.out, dev.q, dev.key_cache, dev.value_cache, dev.block_tables, dev.context_lens,
-                 wl.max_context_len, wl.scale, 0)
+                 wl.max_context_len, wl.scale, 0,
+                 workspace=pa.decode_workspace(dev.q, dev.key_cache, wl.max_context_len, 0))
     torch.cuda.synchronize()
     rs = P.compute_slots(wl.block_tables, wl.block_size, wl.num_blocks, context_lens=wl.context_lens)
     assert np.array_equal(slots.cpu().numpy(), rs)

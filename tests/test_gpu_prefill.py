@@ -101,9 +101,11 @@ def test_prefill_one_query_row_is_decode():
     wl, qs, q = _case("f16", ctx, [1, 1, 1], 4, 4, 128, 16, seed=13)
     got = _run(wl, qs, q)
     out = torch.empty((3, 4, 128), dtype=torch.float16, device="cuda")
-    pa.pa_decode(out, to_torch(q, "f16", "cuda"), to_torch(wl.key_cache, "f16", "cuda"),
-                 to_torch(wl.value_cache, "f16", "cuda"), torch.tensor(wl.block_tables, device="cuda"),
-                 torch.tensor(wl.context_lens, device="cuda"), wl.max_context_len, wl.scale)
+    dq, dk = to_torch(q, "f16", "cuda"), to_torch(wl.key_cache, "f16", "cuda")
+    pa.pa_decode(out, dq, dk, to_torch(wl.value_cache, "f16", "cuda"),
+                 torch.tensor(wl.block_tables, device="cuda"),
+                 torch.tensor(wl.context_lens, device="cuda"), wl.max_context_len, wl.scale,
+                 workspace=pa.decode_workspace(dq, dk, wl.max_context_len))
     torch.cuda.synchronize()
     dec = P.to_f64(from_torch(out, "f16"), "f16")
     BD.assert_close(got, dec, "f16", "prefill row vs decode")

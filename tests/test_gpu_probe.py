@@ -28,7 +28,8 @@ def test_read_probe_reads_every_word_once(tile_kib, tiles):
     want = int(np.bitwise_xor.reduce(host))
     buf = torch.from_numpy(host.view(np.int32)).cuda()
     for order in (None, torch.from_numpy(rng.permutation(tiles).astype(np.int32)).cuda()):
-        sink = pa.pa_read_probe(buf, tile_kib * 1024, order)
+        sink = torch.zeros(pa.PA_READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+        pa.pa_read_probe(buf, tile_kib * 1024, order, sink)
         torch.cuda.synchronize()
         got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
         assert got == want, f"order={'perm' if order is not None else 'index'}: {got:#x} != {want:#x}"

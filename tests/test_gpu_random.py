@@ -92,18 +92,22 @@ def test_random_shapes(case):
     mctx = max(int(wl.context_lens.max()), 1)
     if c["kind"] == "decode":
         pa.pa_decode(dev.out, dev.q, dev.key_cache, dev.value_cache, dev.block_tables,
-                     dev.context_lens, mctx, wl.scale, c["ps"])
+                     dev.context_lens, mctx, wl.scale, c["ps"],
+                     workspace=pa.decode_workspace(dev.q, dev.key_cache, mctx, c["ps"]))
     elif c["kind"] == "append":
         pa.pa_append_decode(dev.out, dev.q, dev.new_key, dev.new_value, dev.key_cache,
                             dev.value_cache, dev.block_tables, dev.context_lens, mctx, wl.scale,
-                            c["ps"])
+                            c["ps"],
+                            workspace=pa.decode_workspace(dev.q, dev.key_cache, mctx, c["ps"]))
     elif c["kind"] == "decode_fp8":
         pa.pa_decode_fp8(dev.out, dev.q, dev.key_cache, dev.value_cache, dev.block_tables,
-                         dev.context_lens, mctx, wl.k_scale, wl.v_scale, wl.scale, c["ps"])
+                         dev.context_lens, mctx, wl.k_scale, wl.v_scale, wl.scale, c["ps"],
+                         workspace=pa.decode_workspace(dev.q, dev.key_cache, mctx, c["ps"]))
     else:
         pa.pa_append_decode_fp8(dev.out, dev.q, dev.new_key, dev.new_value, dev.key_cache,
                                 dev.value_cache, dev.block_tables, dev.context_lens, mctx,
-                                wl.k_scale, wl.v_scale, wl.scale, c["ps"])
+                                wl.k_scale, wl.v_scale, wl.scale, c["ps"],
+                                workspace=pa.decode_workspace(dev.q, dev.key_cache, mctx, c["ps"]))
     torch.cuda.synchronize()
     got = P.to_f64(from_torch(dev.out, wl.dtype), wl.dtype)
     BD.assert_close(got, ref, wl.dtype, c["kind"])

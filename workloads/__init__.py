@@ -49,11 +49,39 @@ def _f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def _f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16 (nearest, ties to even); returns uint16
+    bits.  The same words as ``x.astype(np.float16)`` for every input (NaN
+    becomes 0x7E00), written in integer ufuncs that release the GIL, so the
+    chunked draws convert in parallel (numpy's own float16 cast does not)."""
+    b = x.view(np.uint32)
+    a = b & np.uint32(0x7FFFFFFF)
+    # normal binary16 range: rebias the exponent (127 - 15 = 112) and round
+    # the 23-bit significand to 10 bits; a carry out of the significand moves
+    # into the exponent, and past 65504 the result lands on infinity (0x7C00).
+    n = a - np.uint32(112 << 23)
+    t = n >> np.uint32(13)
+    t &= np.uint32(1)
+    n += t
+    n += np.uint32(0x0FFF)
+    n >>= np.uint32(13)
+    np.minimum(n, np.uint32(0x7C00), out=n)
+    # below 2^-14: a multiple of 2^-24, exact in float32 after scaling by 2^24
+    sub = np.abs(x)
+    sub *= np.float32(2.0 ** 24)
+    np.rint(sub, out=sub)
+    np.copyto(n, sub.astype(np.uint32), where=a < np.uint32(0x38800000))
+    np.copyto(n, np.uint32(0x7E00), where=a > np.uint32(0x7F800000))
+    h = n.astype(np.uint16)
+    h |= (b >> np.uint32(16)).astype(np.uint16) & np.uint16(0x8000)
+    return h
+
+
 def _encode(x32: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return x32
     if dtype == "f16":
-        return x32.astype(np.float16)
+        return _f32_to_f16_bits(x32).view(np.float16)
     if dtype == "bf16":
         return _f32_to_bf16_bits(x32)
     raise ValueError(dtype)
