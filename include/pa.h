@@ -14,9 +14,11 @@
  *
  * Conventions shared by every entry point
  *   - Every array pointer is a DEVICE pointer to memory the caller owns; the
- *     library never allocates, frees or keeps device memory, never
- *     synchronises the host, and launches only on the caller's `stream`
- *     (NULL = the null stream).  Calls return as soon as the work is queued.
+ *     library never allocates, frees or keeps device memory (the one
+ *     exception: the static per-GPU scratch array of pa_decode_noalloc, part
+ *     of the loaded code), never synchronises the host, and launches only on
+ *     the caller's `stream` (NULL = the null stream).  Calls return as soon
+ *     as the work is queued.
  *   - Arrays are dense, row-major, with the shapes given per argument.
  *   - Storage types: PA_F32 (IEEE binary32), PA_F16 (IEEE binary16),
  *     PA_BF16 (bfloat16).  Arithmetic is float32 throughout.
@@ -182,6 +184,34 @@ pa_status_t pa_decode(void *out, const void *q, const void *key_cache, const voi
                       int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                       int32_t partition_size, void *workspace, size_t workspace_bytes,
                       pa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes no workspace: the split-context partials go to
+ * a static device array of PA_NOALLOC_SCRATCH_BYTES (16 MiB) that each GPU the
+ * library runs on holds until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, no hipFree); the first call on a device looks up
+ * that device's copy of the array.
+ *
+ * Arguments and results as for pa_decode (fp32/fp16/bf16 pools), minus
+ * workspace and workspace_bytes.  A split that needs more than
+ * PA_NOALLOC_SCRATCH_BYTES (pa_decode_workspace_size) is refused with
+ * PA_ERR_WORKSPACE_TOO_SMALL before anything is launched; 16 MiB holds, e.g.,
+ * 8 sequences x 32 heads x 64 partitions of a 128-dim head (8.5 MB).
+ * Every call on one GPU shares that GPU's array and leaves its partials
+ * there (nothing in it needs clearing: every partial read is written first
+ * by the same call); calls that overlap on one GPU (different streams, or
+ * host threads) race on it and must be serialised by the caller.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+pa_status_t pa_decode_noalloc(void *out, const void *q, const void *key_cache,
+                              const void *value_cache, const int32_t *block_tables,
+                              const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, float scale, int32_t partition_size,
+                              pa_dtype_t dtype, hipStream_t stream);
 
 /*
  * pa_append_decode -- one decode step in one launch: for every sequence s

@@ -21,6 +21,8 @@ from ._capi import (  # noqa: F401
     pa_append_decode_fp8,
     pa_decode,
     pa_decode_fp8,
+    pa_decode_noalloc,
+    PA_NOALLOC_SCRATCH_BYTES,
     pa_decode_partition_size,
     pa_decode_workspace_size,
     pa_last_error,

@@ -57,6 +57,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.pa_append_decode.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32,
                                      i32, i32, i32, i32, c.c_float, i32, ptr, sz, c.c_int, ptr]
     lib.pa_append_decode.restype = st
+    lib.pa_decode_noalloc.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, i32, i32,
+                                      i32, i32, c.c_float, i32, c.c_int, ptr]
+    lib.pa_decode_noalloc.restype = st
     lib.pa_read_probe.argtypes = [ptr, c.c_int64, c.c_int64, ptr, ptr, ptr]
     lib.pa_read_probe.restype = st
     lib.pa_append_decode_fp8.argtypes = [ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, i32, i32, i32,
@@ -548,4 +551,37 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
         ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(context_lens.data_ptr()),
         S, H, Hkv, D, B, NB, block_tables.shape[1], max_context_len, float(scale),
         partition_size, ws_ptr, ws_bytes, dt, _stream(q)))
+    return out
+
+
+PA_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def pa_decode_noalloc(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, max_context_len: int, scale: float,
+                      partition_size: int = 0) -> torch.Tensor:
+    """pa_decode without a workspace: split-context partials go to the
+    library's static per-GPU scratch (PA_NOALLOC_SCRATCH_BYTES); see
+    include/pa.h.  Calls that overlap on one GPU race on that scratch."""
+    lib = load_library()
+    for n, t in (("out", out), ("q", q), ("key_cache", key_cache), ("value_cache", value_cache),
+                 ("block_tables", block_tables), ("context_lens", context_lens)):
+        _dev(t, n)
+    if q.dtype not in DTYPE_CODES or any(t.dtype != q.dtype for t in (out, key_cache, value_cache)):
+        raise ValueError("q, out and the pools must share one of float32/float16/bfloat16")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    S, H, D = q.shape
+    NB, Hkv, B, D2 = key_cache.shape
+    if D2 != D or tuple(value_cache.shape) != (NB, Hkv, B, D) or tuple(out.shape) != (S, H, D):
+        raise ValueError("shape mismatch between q, out and the pools")
+    if block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables and context_lens must have one row per sequence")
+    _check(lib.pa_decode_noalloc(
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(key_cache.data_ptr()), ctypes.c_void_p(value_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(context_lens.data_ptr()),
+        S, H, Hkv, D, B, NB, block_tables.shape[1], max_context_len, float(scale),
+        partition_size, DTYPE_CODES[q.dtype], _stream(q)))
     return out

@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 
 #include "pa_internal.h"
@@ -254,7 +256,7 @@ pa_status_t decode_impl(void *out, const void *q, const void *key_cache, const v
                         float k_scale, float v_scale, int32_t partition_size, void *workspace,
                         size_t workspace_bytes, pa_dtype_t q_dt, pa_dtype_t kv_dt,
                         hipStream_t stream, const void *new_k = nullptr,
-                        const void *new_v = nullptr) {
+                        const void *new_v = nullptr, bool workspace_is_device = false) {
   Sizes z;
   pa_status_t st = plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                         max_context_len, partition_size, kv_dt, &z);
@@ -285,7 +287,7 @@ pa_status_t decode_impl(void *out, const void *q, const void *key_cache, const v
       return fail(PA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     // The kernels write the partials there: refuse memory the GPU cannot
     // reach (pageable host memory) instead of handing it to them.
-    workspace = const_cast<void *>(device_view(workspace));
+    if (!workspace_is_device) workspace = const_cast<void *>(device_view(workspace));
     if (!workspace)
       return fail(PA_ERR_INVALID_ARGUMENT,
                   "workspace must be device memory or pinned (hipHostMalloc) host memory");
@@ -400,6 +402,88 @@ pa_status_t pa_decode_fp8(void *out, const void *q, const void *key_cache,
                      num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, k_scale, v_scale,
                      partition_size, workspace, workspace_bytes, q_dtype, PA_FP8_E4M3, stream);
+}
+
+}  // extern "C"
+
+// pa_decode_noalloc's workspace: one static device array per GPU, held until
+// the process ends.  Host code never uses the array's own name as an address
+// (on the host it is only a stand-in); it uses the per-device address that
+// hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch address on the device that `stream` belongs to (the current
+// device for the null stream).  The first call on a device makes that device
+// current, looks the address up and restores the caller's device.
+pa_status_t scratch_for(hipStream_t stream, void **ptr) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, std::string("device of the stream: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "device index above 63");
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = -1;
+      e = hipGetDevice(&cur);
+      if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+      if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur >= 0 && cur != dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+      }
+      if (e != hipSuccess || !p)
+        return fail(PA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                    hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode_noalloc(void *out, const void *q, const void *key_cache,
+                              const void *value_cache, const int32_t *block_tables,
+                              const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, float scale, int32_t partition_size,
+                              pa_dtype_t dtype, hipStream_t stream) {
+  if (dtype == PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_noalloc takes PA_F32, PA_F16 or PA_BF16 pools");
+  Sizes z;
+  pa_status_t st = plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_context_len, partition_size, dtype, &z);
+  if (st != PA_OK) return st;
+  if (z.ws_bytes > PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                "this split needs " + std::to_string(z.ws_bytes) +
+                    " bytes of workspace, above the static scratch of " +
+                    std::to_string((size_t)PA_NOALLOC_SCRATCH_BYTES) +
+                    " bytes: use pa_decode with a workspace, or longer partitions");
+  void *ws = nullptr;
+  if (z.ws_bytes > 0 && num_seqs > 0) {
+    st = scratch_for(stream, &ws);
+    if (st != PA_OK) return st;
+  }
+  return decode_impl(out, q, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, 1.f, 1.f, partition_size, ws,
+                     ws ? (size_t)PA_NOALLOC_SCRATCH_BYTES : 0, dtype, dtype, stream, nullptr,
+                     nullptr, /*workspace_is_device=*/true);
 }
 
 }  // extern "C"

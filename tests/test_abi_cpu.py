@@ -276,3 +276,22 @@ def test_decode_refuses_a_workspace_the_gpu_cannot_reach(lib):
     st = _decode(lib, P=16, maxctx=128, ws=ctypes.c_void_p(addr), wsb=need)
     assert st == _capi.PA_ERR_INVALID_ARGUMENT
     assert "workspace" in pa.pa_last_error()
+
+
+def test_noalloc_decode_refuses_a_split_above_its_scratch(lib):
+    """pa_decode_noalloc has a fixed static scratch: a split whose partials
+    need more is refused before anything is looked up or launched."""
+    args = dict(S=64, H=64, Hkv=64, D=128, B=16, NB=8192, MB=2048, maxctx=32768, P=512)
+    need = lib.pa_decode_workspace_size(args["S"], args["H"], args["Hkv"], args["D"], args["B"],
+                                        args["maxctx"], args["P"], F16)
+    assert need > pa.PA_NOALLOC_SCRATCH_BYTES
+    st = lib.pa_decode_noalloc(_p(), _p(), _p(), _p(), _p(), _p(), args["S"], args["H"],
+                               args["Hkv"], args["D"], args["B"], args["NB"], args["MB"],
+                               args["maxctx"], 0.1, args["P"], F16, None)
+    assert st == _capi.PA_ERR_WORKSPACE_TOO_SMALL
+    assert "scratch" in pa.pa_last_error()
+    # invalid shapes are refused as by pa_decode
+    assert lib.pa_decode_noalloc(_p(), _p(), _p(), _p(), _p(), _p(), 2, 8, 3, 128, 16, 64, 8,
+                                 128, 0.1, 0, F16, None) == _capi.PA_ERR_INVALID_ARGUMENT
+    assert lib.pa_decode_noalloc(_p(), _p(), _p(), _p(), _p(), _p(), 2, 8, 8, 128, 16, 64, 8,
+                                 128, 0.1, 0, 3, None) == _capi.PA_ERR_UNSUPPORTED
