@@ -15,7 +15,9 @@ import re
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libpa.so")
+# PA_LIBRARY names another build of the same C ABI (the sanitizer tests load a
+# CPU-only build of the host code through it); by default the in-tree libpa.so.
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_PKG, "libpa.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
 
 (PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP,

@@ -440,12 +440,6 @@ hipError_t launch_gqa_t(const DecodeArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-bool gqa_supported(int kv_dt, int head_dim, int num_heads, int num_kv_heads) {
-  const int G = num_heads / num_kv_heads;
-  return (kv_dt == kF16 || kv_dt == kBF16 || kv_dt == kFP8) &&
-         (head_dim == 64 || head_dim == 128) && G >= 2;
-}
-
 hipError_t launch_decode_gqa(const DecodeArgs &a, int dt, int kv_dt, hipStream_t stream) {
   const bool f8 = kv_dt == kFP8;
   if (!f8 && kv_dt != dt) return hipErrorInvalidValue;

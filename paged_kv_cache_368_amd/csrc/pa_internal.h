@@ -75,8 +75,10 @@ struct PrefillArgs {
   float v_scale;             // E4M3 pools: the V scale, applied to the outputs
 };
 
-// Paged prefill on the matrix cores: fp16/bf16, head_dim 64 or 128.
-int prefill_rows_per_tile();
+// Paged prefill on the matrix cores: fp16/bf16, head_dim 64 or 128; one
+// work-group per tile of kPrefillRows query rows of one (sequence, head).
+constexpr int kPrefillRows = 256;
+inline int prefill_rows_per_tile() { return kPrefillRows; }
 hipError_t launch_prefill(const PrefillArgs &a, int dt, int kv_dt, hipStream_t stream);
 
 hipError_t launch_decode_mha(const DecodeArgs &a, int dt, int kv_dt, hipStream_t stream);
@@ -87,7 +89,10 @@ hipError_t launch_merge(const DecodeArgs &a, int dt, hipStream_t stream);
 // num_heads / num_kv_heads >= 2.  One work item per (sequence, kv head,
 // tile of up to kGqaTile query heads, partition) instead of per query head.
 constexpr int kGqaTile = 16;
-bool gqa_supported(int kv_dt, int head_dim, int num_heads, int num_kv_heads);
+inline bool gqa_supported(int kv_dt, int head_dim, int num_heads, int num_kv_heads) {
+  return (kv_dt == kF16 || kv_dt == kBF16 || kv_dt == kFP8) &&
+         (head_dim == 64 || head_dim == 128) && num_heads / num_kv_heads >= 2;
+}
 hipError_t launch_decode_gqa(const DecodeArgs &a, int dt, int kv_dt, hipStream_t stream);
 
 hipError_t launch_cache_write(const void *key, const void *value, void *key_cache,

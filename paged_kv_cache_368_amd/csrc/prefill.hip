@@ -442,7 +442,7 @@ hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-int prefill_rows_per_tile() { return kRows; }
+static_assert(kRows == kPrefillRows, "the host sizes the grid with kPrefillRows");
 
 hipError_t launch_prefill(const PrefillArgs &a, int dt, int kv_dt, hipStream_t stream) {
   const bool f8 = kv_dt == kFP8;

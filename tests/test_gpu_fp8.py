@@ -222,3 +222,162 @@ def test_prefill_fp8_matches_oracle(name, kw, qt):
     ref = P.paged_prefill_fp8(q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens,
                               qs, B, wl.scale, qt, wl.k_scale, wl.v_scale, Hkv)
     BD.assert_close(got, ref, qt, f"prefill fp8 {name} {qt}")
+
+
+# ---------------------------------------------------------------------------
+# the quantiser where float32 and exact division disagree; pools holding every
+# non-NaN code with scales that are not powers of two; the bench's fp8 prefill
+# at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("src", ["f32", "f16", "bf16"])
+def test_cache_write_fp8_float32_division_cases(src):
+    """Rows made of inputs whose float32 quotient x / scale rounds to another
+    code than the exact quotient (tests/_fp8_cases.py): the kernel stores the
+    oracle's codes, which follow the float32 quotient (pinned on the CPU)."""
+    import tests._fp8_cases as FP8C
+    _say(f"cache_write_fp8 division cases from {src}")
+    Hkv, B, D, NB = 2, 16, 128, 8
+    kx = [x for x, _, _ in FP8C.divergent_inputs(src, FP8C.K_SCALE)]
+    vx = [x for x, _, _ in FP8C.divergent_inputs(src, FP8C.V_SCALE)]
+    per_token = Hkv * D
+
+    def rows(xs, stream):
+        vals = np.array(xs + [-x for x in xs], np.float64)
+        T = -(-len(vals) // per_token) + 1
+        fill = P.to_f64(normal_array(31, stream, (T * per_token,), src), src)
+        fill[:len(vals)] = vals
+        flat = fill.astype(np.float32)
+        if src == "f16":
+            return flat.astype(np.float16).reshape(T, Hkv, D)
+        if src == "bf16":
+            return (flat.view(np.uint32) >> 16).astype(np.uint16).reshape(T, Hkv, D)
+        return flat.reshape(T, Hkv, D)
+
+    key, value = rows(kx, 1), rows(vx, 2)
+    T = max(len(key), len(value))
+    key = np.concatenate([key] + [key[:1]] * (T - len(key)))
+    value = np.concatenate([value] + [value[:1]] * (T - len(value)))
+    assert P.to_f64(key, src).reshape(-1)[:len(kx)].tolist() == kx     # exact in the source type
+    slots = np.random.default_rng(8).choice(NB * B, T, replace=False).astype(np.int64)
+    kc = np.full((NB, Hkv, B, D), 0x55, np.uint8)
+    vc = kc.copy()
+    ref_k, ref_v = kc.copy(), vc.copy()
+    P.cache_write_fp8(ref_k, ref_v, key, value, slots, B, src, FP8C.K_SCALE, FP8C.V_SCALE)
+    dk, dv = to_torch(kc, "fp8", "cuda"), to_torch(vc, "fp8", "cuda")
+    pa.pa_cache_write_fp8(to_torch(key, src, "cuda"), to_torch(value, src, "cuda"), dk, dv,
+                          torch.tensor(slots, device="cuda"), FP8C.K_SCALE, FP8C.V_SCALE)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_torch(dk, "fp8"), ref_k), "K codes"
+    assert np.array_equal(from_torch(dv, "fp8"), ref_v), "V codes"
+
+
+# every non-NaN code in the pools; K and V scales that are not powers of two
+# (K values up to 448 * 0.0371 = 16.6, V up to 448 * 0.0052 = 2.3)
+ALL_CODES = dict(kv_codes="all", kv_scale=0.0371, v_scale=0.0052)
+ALL_CODE_CASES = [FP8_CASES[0], FP8_CASES[3], FP8_CASES[4], FP8_CASES[7]]
+
+
+@pytest.mark.parametrize("qt", ["f16", "bf16"])
+@pytest.mark.parametrize("name,kw", ALL_CODE_CASES, ids=[c[0] for c in ALL_CODE_CASES])
+def test_decode_fp8_all_codes(name, kw, qt):
+    _say(f"fp8 decode all codes {name} {qt}")
+    wl = build(f"fp8all_{name}", qt, kw["ctx"], kw["H"], kw["Hkv"], kw["D"], kw["B"], seed=27,
+               pool="choice", pool_factor=1.5, value_scale=0.5, kv_dtype="fp8", **ALL_CODES)
+    live = wl.key_cache[wl.key_cache != 0x7F]
+    assert len(np.unique(live)) == 254 or live.size < 20000
+    ref = _oracle(wl)
+    for ps in (0, 64):
+        got = _fp8_decode(wl, partition_size=ps)
+        BD.assert_close(got, ref, qt, f"{name} all codes, partition {ps}")
+
+
+@pytest.mark.parametrize("qt", ["f16", "bf16"])
+@pytest.mark.parametrize("name,kw", ALL_CODE_CASES, ids=[c[0] for c in ALL_CODE_CASES])
+def test_append_decode_fp8_all_codes(name, kw, qt):
+    """The one-launch step over all-code pools with non-power-of-two scales:
+    the new rows' codes bit-exact, outputs within the decode bars."""
+    _say(f"fp8 append all codes {name} {qt}")
+    wl = build(f"fp8allapp_{name}", qt, kw["ctx"], kw["H"], kw["Hkv"], kw["D"], kw["B"],
+               seed=28, pool="choice", pool_factor=1.5, value_scale=0.5, kv_dtype="fp8",
+               **ALL_CODES)
+    slots = P.compute_slots(wl.block_tables, wl.block_size, wl.num_blocks,
+                            context_lens=wl.context_lens)
+    kc, vc = wl.key_cache.copy(), wl.value_cache.copy()
+    P.cache_write_fp8(kc, vc, wl.new_key, wl.new_value, slots, wl.block_size, qt, wl.k_scale,
+                      wl.v_scale)
+    ref = P.paged_decode_fp8(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.block_size,
+                             wl.scale, qt, wl.k_scale, wl.v_scale, wl.num_kv_heads)
+    dev = to_device(wl)
+    pa.pa_append_decode_fp8(dev.out, dev.q, dev.new_key, dev.new_value, dev.key_cache,
+                            dev.value_cache, dev.block_tables, dev.context_lens,
+                            wl.max_context_len, wl.k_scale, wl.v_scale, wl.scale, 64,
+                            workspace=pa.decode_workspace(dev.q, dev.key_cache,
+                                                          wl.max_context_len, 64))
+    torch.cuda.synchronize()
+    BD.assert_close(P.to_f64(from_torch(dev.out, qt), qt), ref, qt, f"{name} all codes")
+    assert np.array_equal(from_torch(dev.key_cache, "fp8"), kc), "K codes"
+    assert np.array_equal(from_torch(dev.value_cache, "fp8"), vc), "V codes"
+
+
+@pytest.mark.parametrize("qt", ["f16", "bf16"])
+@pytest.mark.parametrize("name,kw", PF8_CASES, ids=[c[0] for c in PF8_CASES])
+def test_prefill_fp8_all_codes(name, kw, qt):
+    ctx, H, Hkv, D, B = kw["ctx"], kw["H"], kw["Hkv"], kw["D"], kw["B"]
+    qlens = kw["qlens"] or ctx
+    _say(f"prefill fp8 all codes {name} {qt}")
+    wl = build("pf8all", qt, ctx, H, Hkv, D, B, seed=41 + D + B, pool="choice",
+               pool_factor=1.3, kv_dtype="fp8", **ALL_CODES)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = normal_array(42, 40, (int(qs[-1]), H, D), qt, 0.5)
+    tdt = torch.float16 if qt == "f16" else torch.bfloat16
+    out = torch.full((int(qs[-1]), H, D), float("inf"), dtype=tdt, device="cuda")
+    pa.pa_prefill_fp8(out, to_torch(q, qt, "cuda"), to_torch(wl.key_cache, "fp8", "cuda"),
+                      to_torch(wl.value_cache, "fp8", "cuda"),
+                      torch.tensor(wl.block_tables, device="cuda"),
+                      torch.tensor(wl.context_lens, device="cuda"), torch.tensor(qs, device="cuda"),
+                      int(max(qlens)), wl.max_context_len, wl.k_scale, wl.v_scale, wl.scale)
+    torch.cuda.synchronize()
+    got = P.to_f64(from_torch(out, qt), qt)
+    ref = P.paged_prefill_fp8(q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens,
+                              qs, B, wl.scale, qt, wl.k_scale, wl.v_scale, Hkv)
+    BD.assert_close(got, ref, qt, f"prefill fp8 all codes {name} {qt}")
+
+
+@pytest.mark.parametrize("prefix", [0, 1536])
+def test_prefill_fp8_full_size_sampled(prefix):
+    """The inputs and launch ``bench.py --op prefill --kv fp8`` times: 8
+    LLaMA-7B-shaped prompts of 2048 tokens over E4M3 pools, whole or the last
+    512 after a cached 1536-token prefix; sampled (row, head) pairs against
+    the oracle: both ends of every 256-row tile of the first and last
+    sequences, every sequence's first and last row, and random ones."""
+    import bench
+    _say(f"prefill fp8 full size, prefix {prefix}")
+    wl, qs, q = bench.prefill_workload(prefix, fp8=True)
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    n = wl.max_context_len
+    L = n - prefix
+    out = torch.full((S * L, H, D), float("inf"), dtype=torch.float16, device="cuda")
+    pa.pa_prefill_fp8(out, to_torch(q, "f16", "cuda"), to_torch(wl.key_cache, "fp8", "cuda"),
+                      to_torch(wl.value_cache, "fp8", "cuda"),
+                      torch.tensor(wl.block_tables, device="cuda"),
+                      torch.tensor(wl.context_lens, device="cuda"), torch.tensor(qs, device="cuda"),
+                      L, n, wl.k_scale, wl.v_scale, wl.scale)
+    torch.cuda.synchronize()
+    got = P.to_f64(from_torch(out, "f16"), "f16")
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(90 + prefix)
+    rows = set()
+    for s in (0, S - 1):
+        for t0 in range(0, L, 256):
+            rows.update({(s * L + t0, int(rng.integers(H))),
+                         (s * L + min(t0 + 255, L - 1), int(rng.integers(H)))})
+    for s in range(S):
+        rows.update({(s * L, int(rng.integers(H))), (s * L + L - 1, int(rng.integers(H)))})
+    rows.update((int(rng.integers(S * L)), int(rng.integers(H))) for _ in range(48))
+    rows = sorted(rows)
+    ref = P.paged_prefill_fp8(q, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lens,
+                              qs, wl.block_size, wl.scale, "f16", wl.k_scale, wl.v_scale,
+                              wl.num_kv_heads, rows)
+    idx = tuple(np.array(rows).T)
+    BD.assert_close(got[idx], ref[idx], "f16", f"prefill fp8 full size, prefix {prefix}")

@@ -178,11 +178,16 @@ def _prefill_pos_plus_one(q, kc, vc, bt, cl, qs, b, scale, dtype, hkv=None, rows
     return out
 
 
+def _quantize_exact_division(x_f32, scale):
+    q = np.asarray(x_f32, dtype=np.float32).astype(np.float64) / float(np.float32(scale))
+    return _orig["e4m3_encode"](q)
+
+
 MUTANTS = {
     "paged_prefill": [_prefill_top_left, _prefill_not_causal, _prefill_pos_plus_one],
     "e4m3_decode": [_e4m3_bias8, _e4m3_no_subnormals],
     "e4m3_encode": [_e4m3_truncate, _e4m3_ties_up],
-    "quantize_e4m3": [_quantize_times_scale],
+    "quantize_e4m3": [_quantize_times_scale, _quantize_exact_division],
     "paged_decode_fp8": [_fp8_decode_no_v_scale],
     "copy_blocks": [_copy_reversed, _copy_no_bounds],
     "num_required_blocks": [_floor_blocks],

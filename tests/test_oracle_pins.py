@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle.paged as P
+import tests._fp8_cases as FP8C
 from workloads import build, make_workload
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -373,6 +374,29 @@ def test_workload_tiny_shape(idx):
     assert wl.key_cache.shape == (64, 8, 16, 64)
 
 
+def test_workload_f16_rounding_is_numpys_cast():
+    """The generators' float32 -> fp16 rounding (integer ufuncs, so chunks
+    convert in parallel) gives numpy's own cast's words for every non-NaN
+    float32: random bit patterns, the subnormal and overflow boundaries, and
+    every float32 around the smallest normal."""
+    import warnings
+
+    import workloads as W
+    rng = _rng(44)
+    pats = [rng.integers(0, 2**32, 1 << 20, dtype=np.uint64).astype(np.uint32),
+            np.arange(0x33000000, 0x39000000, 97, dtype=np.uint32),
+            np.arange(0x477F0000, 0x7F800001, 4099, dtype=np.uint32)]
+    for p in pats:
+        for x in (p.view(np.float32), -p.view(np.float32)):
+            with warnings.catch_warnings():
+                warnings.simplefilter("ignore")
+                want = x.astype(np.float16).view(np.uint16)
+            got = W._f32_to_f16_bits(x)
+            keep = ~np.isnan(x)
+            assert np.array_equal(got[keep], want[keep])
+            assert ((got[~keep] & 0x7FFF) == 0x7E00).all()
+
+
 def test_workload_reproducible_and_prefix_shared():
     a = build("t", "bf16", [70, 130], 4, 2, 16, 16, seed=3, shared_prefix_tokens=32)
     b = build("t", "bf16", [70, 130], 4, 2, 16, 16, seed=3, shared_prefix_tokens=32)
@@ -513,6 +537,24 @@ def test_pin_fp8_cache_write_quantises_with_pool_scale():
     touched = np.zeros((NB, B), bool)
     touched[5 // B, 5 % B] = touched[22 // B, 22 % B] = True
     assert (kc.transpose(0, 2, 1, 3)[~touched] == 0x55).all()
+
+
+def test_pin_fp8_quantiser_divides_in_float32():
+    """Reading F1: the stored code is the one nearest float32(x) / float32(s),
+    the quotient rounded to float32 (the kernel's precision).  On inputs
+    where the exact quotient (float64) lands on another code, the oracle
+    must give the float32 quotient's code (brute force over torch's E4M3
+    table), for both signs and for inputs of every source type."""
+    for src in ("f32", "f16", "bf16"):
+        for scale in (FP8C.K_SCALE, FP8C.V_SCALE):
+            cases = FP8C.divergent_inputs(src, scale)
+            assert len(cases) >= 8, f"only {len(cases)} divergent inputs for {src} at {scale}"
+            xs = np.array([x for x, _, _ in cases] + [-x for x, _, _ in cases], np.float32)
+            want32 = [c32 for _, c32, _ in cases] + [c32 | 0x80 for _, c32, _ in cases]
+            want64 = [c64 for _, _, c64 in cases] + [c64 | 0x80 for _, _, c64 in cases]
+            got = P.quantize_e4m3(xs, scale)
+            assert got.tolist() == want32, f"{src} at scale {scale}"
+            assert all(g != w for g, w in zip(got.tolist(), want64))
 
 
 # --------------------------------------------------------------------------

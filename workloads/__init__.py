@@ -14,8 +14,10 @@ Recipe (every array is reproducible from ``seed`` alone):
   come from ``SeedSequence(seed, spawn_key=(array_id, chunk))`` -- so the result
   does not depend on how many threads draw it.  They are multiplied by the
   workload's value scale (0.5 for the LLaMA-7B shape, else 1) and rounded to
-  the storage type with round-to-nearest-even: numpy's cast for fp16, a bit
-  rounding of the float32 word for bf16 (stored as raw ``uint16``).
+  the storage type with round-to-nearest-even: integer rounding of the
+  float32 word to fp16 (the same words as numpy's cast) or to bf16 (stored
+  as raw ``uint16``).
+* E4M3 pools hold random codes drawn as bit patterns (see ``e4m3_codes``).
 * Pools are ``[num_blocks][num_kv_heads][block_size][head_dim]``.  Every slot
   that no sequence's context covers (whole unused blocks and the tail of each
   sequence's last block) is set to NaN, so any kernel that lets a masked slot
@@ -131,11 +133,13 @@ _E4M3_EXP_TABLE = np.repeat(np.arange(2, 10, dtype=np.uint8),
                             [1, 2, 4, 8, 14, 14, 6, 1])          # 50 entries
 
 
-def e4m3_codes(seed: int, stream: int, shape, threads: int | None = None) -> np.ndarray:
+def e4m3_codes(seed: int, stream: int, shape, threads: int | None = None,
+               all_codes: bool = False) -> np.ndarray:
     """Random E4M3 storage codes (uint8): random sign and mantissa bits and an
-    exponent field drawn from ``_E4M3_EXP_TABLE``.  Codes are drawn directly
-    as bit patterns (no value is quantised here); NaN codes never occur.
-    Chunked and seeded per chunk like ``normal_array``."""
+    exponent field drawn from ``_E4M3_EXP_TABLE``; with ``all_codes``, every
+    one of the 254 non-NaN codes (subnormals through +-448) equally likely.
+    Codes are drawn directly as bit patterns (no value is quantised here); NaN
+    codes never occur.  Chunked and seeded per chunk like ``normal_array``."""
     n = int(np.prod(shape)) if len(shape) else 1
     out = np.empty(n, dtype=np.uint8)
     nchunks = (n + CHUNK - 1) // CHUNK
@@ -143,6 +147,10 @@ def e4m3_codes(seed: int, stream: int, shape, threads: int | None = None) -> np.
     def fill(c: int) -> None:
         lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
         g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(stream, c))))
+        if all_codes:
+            r = g.integers(0, 254, size=hi - lo, dtype=np.uint8)        # 0..253
+            out[lo:hi] = r + (r >= 0x7F).astype(np.uint8)                # skip 0x7F; 0xFF unreachable
+            return
         e = _E4M3_EXP_TABLE[g.integers(0, len(_E4M3_EXP_TABLE), size=hi - lo, dtype=np.uint8)]
         sm = g.integers(0, 16, size=hi - lo, dtype=np.uint8)       # sign bit | 3 mantissa bits
         out[lo:hi] = ((sm & 8) << 4) | (e << 3) | (sm & 7)
@@ -234,14 +242,17 @@ def build(name: str, dtype: str, ctx, num_heads: int, num_kv_heads: int, head_di
           block_size: int, seed: int, pool: str = "permutation", pool_factor: float = 1.0,
           value_scale: float = 1.0, shared_prefix_tokens: int = 0, partition_size: int = 0,
           num_blocks: int | None = None, cw_tokens: int = 0, notes: dict | None = None,
-          kv_dtype: str | None = None, kv_scale: float = 1.0) -> Workload:
+          kv_dtype: str | None = None, kv_scale: float = 1.0, v_scale: float | None = None,
+          kv_codes: str = "normal") -> Workload:
     """Assemble a workload from sizes.
 
     ``pool``: "permutation" -- ids are consecutive slices of a random
     permutation of ``num_blocks`` ids; "choice" -- ids drawn without replacement
     from a pool ``pool_factor`` times the blocks needed.  With
     ``shared_prefix_tokens`` the first ``shared_prefix_tokens / block_size``
-    table entries of every sequence hold the same physical ids.
+    table entries of every sequence hold the same physical ids.  E4M3 pools
+    (``kv_dtype="fp8"``): scales ``kv_scale`` for K and ``v_scale`` (default
+    ``kv_scale``) for V; ``kv_codes="all"`` draws every non-NaN code equally.
     """
     assert dtype in DTYPES
     ctx = np.asarray(ctx, dtype=np.int32)
@@ -282,8 +293,8 @@ def build(name: str, dtype: str, ctx, num_heads: int, num_kv_heads: int, head_di
     H, Hkv, D = num_heads, num_kv_heads, head_dim
     q = normal_array(seed, _STREAM["q"], (S, H, D), dtype, value_scale)
     if kv_dtype == "fp8":
-        kc = e4m3_codes(seed, _STREAM["k"], (NB, Hkv, B, D))
-        vc = e4m3_codes(seed, _STREAM["v"], (NB, Hkv, B, D))
+        kc = e4m3_codes(seed, _STREAM["k"], (NB, Hkv, B, D), all_codes=kv_codes == "all")
+        vc = e4m3_codes(seed, _STREAM["v"], (NB, Hkv, B, D), all_codes=kv_codes == "all")
     else:
         kc = normal_array(seed, _STREAM["k"], (NB, Hkv, B, D), dtype, value_scale)
         vc = normal_array(seed, _STREAM["v"], (NB, Hkv, B, D), dtype, value_scale)
@@ -295,7 +306,8 @@ def build(name: str, dtype: str, ctx, num_heads: int, num_kv_heads: int, head_di
                   key_cache=kc, value_cache=vc, new_key=nk, new_value=nv,
                   scale=1.0 / math.sqrt(D), partition_size=partition_size, seed=seed,
                   notes=dict(notes or {}), kv_dtype=kv_dtype,
-                  k_scale=kv_scale if kv_dtype else 1.0, v_scale=kv_scale if kv_dtype else 1.0)
+                  k_scale=kv_scale if kv_dtype else 1.0,
+                  v_scale=(kv_scale if v_scale is None else v_scale) if kv_dtype else 1.0)
     if cw_tokens:
         wl.cw_slots = rng.choice(NB * B, cw_tokens, replace=False).astype(np.int64)
         wl.cw_key = normal_array(seed, _STREAM["cw_k"], (cw_tokens, Hkv, D), dtype, value_scale)
