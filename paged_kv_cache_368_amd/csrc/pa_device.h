@@ -84,6 +84,17 @@ __device__ __forceinline__ int group_on_xcd(int b, int n, int G) {
   return blk * span + x * G + j;               // head j of group blk * 8 + x
 }
 
+// XCD-major order of n independent items: the hardware hands work-groups to
+// the XCDs round-robin (XCD = index % 8), so giving XCD x the consecutive
+// items x*per .. x*per+per-1 (per = n / 8) keeps neighbouring items, e.g. the
+// pieces of one block, on one XCD and next to each other in its dispatch
+// order.  Items past the last whole 8*per keep the identity mapping.
+__device__ __forceinline__ long long xcd_major(long long b, long long n) {
+  const long long per = n / 8;
+  if (b >= per * 8) return b;
+  return (b % 8) * per + b / 8;
+}
+
 // Round float32 to the storage type, nearest-even; returns the storage bits.
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;
