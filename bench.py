@@ -756,6 +756,24 @@ def bench_cache_write(args) -> dict:
         out[name] = (T, mean, moved)
     T, t, moved = out["prompt"]
     Ts, ts, moved_s = out["step"]
+    # The same kernel and bytes with the prompt's rows going to sorted random
+    # slots and to consecutive slots: how much of the time the scattered
+    # destinations themselves cost (the rows are written 256 B at a time).
+    order = {}
+    key = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    val = torch.empty_like(key).normal_(generator=g)
+    rnd = torch.randperm(NB * B, device="cuda", generator=g)[:T].to(torch.int64)
+    for name, slots in (("sorted_random_slots", torch.sort(rnd).values),
+                        ("consecutive_slots", torch.arange(T, dtype=torch.int64, device="cuda"))):
+        for _ in range(args.warmup):
+            pa.pa_cache_write(key, val, kc, vc, slots)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            pa.pa_cache_write(key, val, kc, vc, slots)
+        b.record()
+        torch.cuda.synchronize()
+        order[name + "_gbps"] = moved / (a.elapsed_time(b) / args.steps * 1e-3) / 1e9
     return {
         "metric": "KV cache write (pa_cache_write): GB/s of rows read + written into scattered slots",
         "value": moved / t / 1e9, "unit": "GB/s (read+write)", "n_gpus": 1, "steps": args.steps,
@@ -769,6 +787,7 @@ def bench_cache_write(args) -> dict:
                      "kernel": "cache_write_kernel", "bytes_per_launch": moved,
                      "mean_launch_us": t * 1e6},
         "decode_step_write": {"tokens": Ts, "mean_us": ts * 1e6, "gbps": moved_s / ts / 1e9},
+        "slot_order_reference": order,
         "cpu_baseline": cpu,
     }
 

@@ -254,23 +254,43 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
       const int tc = w0 + k * kCh;
       if (wrows == 0 || tc > wlast) return;      // uniform: the chunk is after this wave's rows
       const bool diag = tc + kCh - 1 > wpos0;
+      // Every operand read of the chunk is issued first (K in the A layout,
+      // V transposed; V does not depend on the weights), so their LDS
+      // latency overlaps; then the four independent score accumulations
+      // (two token tiles x two subtiles) interleave on the matrix cores.
+      u32x4 ka[2][KI];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < KI; ++i) ka[tt][i] = *reinterpret_cast<const u32x4 *>(sk + k_addr(tt, i));
+      u32x4 vf[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(sv + v_addr(0, n)));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(sv + v_addr(1, n)));
+        const u32x2 w0v = __builtin_bit_cast(u32x2, v0), w1v = __builtin_bit_cast(u32x2, v1);
+        vf[n] = u32x4{w0v.x, w0v.y, w1v.x, w1v.y};
+      }
+      f32x4 acc[2][kSub];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) acc[tt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < KI; ++i)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int u = 0; u < kSub; ++u) acc[tt][u] = mfma_k32<DT>(ka[tt][i], qf[u][i], acc[tt][u]);
       float sc[kSub][2][4];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        f32x4 acc[kSub];
-#pragma unroll
-        for (int u = 0; u < kSub; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < KI; ++i) {
-          const u32x4 ka = *reinterpret_cast<const u32x4 *>(sk + k_addr(tt, i));
-#pragma unroll
-          for (int u = 0; u < kSub; ++u) acc[u] = mfma_k32<DT>(ka, qf[u][i], acc[u]);
-        }
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int u = 0; u < kSub; ++u)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc[u][tt][r] = acc[u][r] * a.scale_log2;
-      }
+          for (int r = 0; r < 4; ++r) sc[u][tt][r] = acc[tt][u][r] * a.scale_log2;
       if (diag) {
 #pragma unroll
         for (int u = 0; u < kSub; ++u)
@@ -318,16 +338,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(sv + v_addr(0, n)));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(sv + v_addr(1, n)));
-        const u32x2 w0v = __builtin_bit_cast(u32x2, v0), w1v = __builtin_bit_cast(u32x2, v1);
-        const u32x4 vf = {w0v.x, w0v.y, w1v.x, w1v.y};
 #pragma unroll
         for (int u = 0; u < kSub; ++u) {
-          o[u][n] = mfma_k32<DT>(pa_hi[u], vf, o[u][n]);
-          if constexpr (DT == kBF16) o[u][n] = mfma_k32<DT>(pa_lo[u], vf, o[u][n]);
+          o[u][n] = mfma_k32<DT>(pa_hi[u], vf[n], o[u][n]);
+          if constexpr (DT == kBF16) o[u][n] = mfma_k32<DT>(pa_lo[u], vf[n], o[u][n]);
         }
       }
     };
