@@ -362,17 +362,20 @@ void decode_gqa_kernel(DecodeArgs a) {
     }
   };
 
-  constexpr int NBUF = 2;
+  // Software pipeline over NBUF register buffers: while chunk k is consumed,
+  // chunks k+1 .. k+NBUF-1 are in flight.
+  constexpr int NBUF = kGqaBuffers;
   u32x4 kb[NBUF][VL], vb[NBUF][VL];
   if (nch_w > 0) {
     const int last = nch_w - 1;
-    load(kb[0], vb[0], 0, last);
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) load(kb[i], vb[i], i, last);
     for (int k0 = 0; k0 < nch_w; k0 += NBUF) {
 #pragma unroll
       for (int i = 0; i < NBUF; ++i) {
         const int k = k0 + i;
         if (k >= nch_w) break;
-        load(kb[(i + 1) % NBUF], vb[(i + 1) % NBUF], k + 1, last);
+        load(kb[(i + NBUF - 1) % NBUF], vb[(i + NBUF - 1) % NBUF], k + NBUF - 1, last);
         consume(kb[i], vb[i], t0 + (wave + NW * k) * kChunk, t1);
       }
     }

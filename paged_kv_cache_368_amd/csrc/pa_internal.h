@@ -31,6 +31,7 @@ constexpr int kDecodeWaves = 4;       // waves per decode work-group
 constexpr int kDecodeBuffers = 2;     // K/V chunk buffers in flight per wave
 constexpr int kDecodeBuffersFp8 = 2;  // the same for 8-bit pools
 constexpr int kGqaWaves = 4;          // waves per grouped-query work-group
+constexpr int kGqaBuffers = 2;        // K/V chunk buffers per grouped-query wave
 constexpr int kMaxPartBlocks = kMaxPartition / 16;
 
 struct DecodeArgs {
