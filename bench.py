@@ -61,45 +61,50 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # sources it was taken on (``sources`` = kernel_source_digest()); any change
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
+    "longctx_prefix_f16/B64/P512/append": {
+        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
+        "fetch_kib": 1984810.125 + 4248.875, "fetch_scale": 1048576 / 524315.812,
+        "write_kib": 9344.000 + 64.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
+    "tiny_f32/B16/P256/append": {
+        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
+        "fetch_kib": 901.333, "fetch_scale": 1048576 / 524308.500,
+        "write_kib": 24.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
     "llama7b_f16/B16/P4096/append": {
-        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
-        "fetch_kib": 328576.453, "fetch_scale": 1048576 / 524315.062,
+        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
+        "fetch_kib": 328573.896, "fetch_scale": 1048576 / 524307.500,
         "write_kib": 768.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
-    "gqa70b_bf16/B16/P2048/append": {
-        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
-        "fetch_kib": 103368.062 + 601.500, "fetch_scale": 1048576 / 524306.875,
-        "write_kib": 1104.094 + 256.000, "write_scale": 1048576 / 1048576.000,
-        "profile": "profiles/decode_counters_all_workloads.md"},
-    "llama7b_fp8kv/B16/P4096/append": {
-        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
-        "fetch_kib": 154700.281, "fetch_scale": 1048576 / 524307.312,
-        "write_kib": 512.000, "write_scale": 1048576 / 1048576.000,
-        "profile": "profiles/decode_counters_all_workloads.md"},
-    "gqa70b_fp8kv/B16/P1024/append": {
-        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
-        "fetch_kib": 49056.328 + 969.500, "fetch_scale": 1048576 / 524306.875,
-        "write_kib": 1824.062 + 256.000, "write_scale": 1048576 / 1048576.000,
-        "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B16/P4096/append": {
-        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
-        "fetch_kib": 1311912.984, "fetch_scale": 1048576 / 524310.750,
+        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
+        "fetch_kib": 1311896.969, "fetch_scale": 1048576 / 524314.250,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B32/P4096/append": {
-        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
-        "fetch_kib": 1311845.578, "fetch_scale": 1048576 / 524306.938,
+        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
+        "fetch_kib": 1311832.167, "fetch_scale": 1048576 / 524306.750,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B64/P4096/append": {
-        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
-        "fetch_kib": 1311812.031, "fetch_scale": 1048576 / 524307.062,
+        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
+        "fetch_kib": 1311800.521, "fetch_scale": 1048576 / 524306.750,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
-    "longctx_prefix_f16/B64/P512/append": {
-        "sources": "aa6191a74b2ca8badd921cfcfd9d6a507b3c4024ebef3f3b336df453ef6efeb8",
-        "fetch_kib": 1985073.734 + 4249.062, "fetch_scale": 1048576 / 524318.750,
-        "write_kib": 9344.000 + 64.000, "write_scale": 1048576 / 1048576.000,
+    "gqa70b_bf16/B16/P2048/append": {
+        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
+        "fetch_kib": 103365.854 + 601.333, "fetch_scale": 1048576 / 524315.250,
+        "write_kib": 1104.245 + 256.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
+    "llama7b_fp8kv/B16/P4096/append": {
+        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
+        "fetch_kib": 154699.083, "fetch_scale": 1048576 / 524308.188,
+        "write_kib": 512.000, "write_scale": 1048576 / 1048576.000,
+        "profile": "profiles/decode_counters_all_workloads.md"},
+    "gqa70b_fp8kv/B16/P1024/append": {
+        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
+        "fetch_kib": 49056.188 + 969.333, "fetch_scale": 1048576 / 524307.750,
+        "write_kib": 1824.083 + 256.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
 }
 
