@@ -7,7 +7,8 @@
 // what the decode kernels read, one (block, kv head) tile of K or V at a
 // time) or in index order when order is NULL.  Each wave reads a contiguous
 // run of the ordered pieces (1 KB each: one 16-byte non-temporal load per
-// lane), sixteen pieces in flight.  Measured on MI355X against interleaved
+// lane), sixteen pieces in flight (the waves past the end of a small buffer
+// read nothing).  Measured on MI355X against interleaved
 // assignments, fewer pieces in flight and other grid sizes, this shape read
 // fastest in both orders (interleaving with four in flight, its earlier
 // form, read random 4 KB tiles 7% slower).  Each work-group writes the XOR
@@ -33,10 +34,13 @@ __global__ __launch_bounds__(kProbeWaves * 64) void read_probe_kernel(
   const long long per_tile = tile_bytes >> 10;
   const long long total = num_tiles * per_tile;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  // Each wave takes its own contiguous range of the ordered pieces; the
-  // (tile, piece) position advances by one per load (a division per load
-  // made the probe ALU-bound).
-  const long long per_wave = (total + nwaves - 1) / nwaves;
+  // Each wave takes its own contiguous range of the ordered pieces, a whole
+  // number of batches of kProbeUnroll, so that a small buffer keeps sixteen
+  // loads in flight per wave on fewer waves rather than one load each on
+  // all of them; the (tile, piece) position advances by one per load (a
+  // division per load made the probe ALU-bound).
+  const long long per_wave =
+      ((total + nwaves - 1) / nwaves + kProbeUnroll - 1) / kProbeUnroll * kProbeUnroll;
   const long long first = wave * per_wave;
   const long long end = min(total, first + per_wave);
   long long t = first / per_tile;
