@@ -62,49 +62,49 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
     "longctx_prefix_f16/B64/P512/append": {
-        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
-        "fetch_kib": 1984810.125 + 4248.875, "fetch_scale": 1048576 / 524315.812,
+        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
+        "fetch_kib": 1984879.240 + 4257.667, "fetch_scale": 1048576 / 524316.625,
         "write_kib": 9344.000 + 64.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "tiny_f32/B16/P256/append": {
-        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
-        "fetch_kib": 901.333, "fetch_scale": 1048576 / 524308.500,
+        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
+        "fetch_kib": 901.333, "fetch_scale": 1048576 / 524307.938,
         "write_kib": 24.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama7b_f16/B16/P4096/append": {
-        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
-        "fetch_kib": 328573.896, "fetch_scale": 1048576 / 524307.500,
+        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
+        "fetch_kib": 328573.740, "fetch_scale": 1048576 / 524307.375,
         "write_kib": 768.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B16/P4096/append": {
-        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
-        "fetch_kib": 1311896.969, "fetch_scale": 1048576 / 524314.250,
+        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
+        "fetch_kib": 1311896.458, "fetch_scale": 1048576 / 524314.875,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B32/P4096/append": {
-        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
-        "fetch_kib": 1311832.167, "fetch_scale": 1048576 / 524306.750,
+        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
+        "fetch_kib": 1311832.521, "fetch_scale": 1048576 / 524307.500,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B64/P4096/append": {
-        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
-        "fetch_kib": 1311800.521, "fetch_scale": 1048576 / 524306.750,
+        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
+        "fetch_kib": 1311800.135, "fetch_scale": 1048576 / 524307.750,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "gqa70b_bf16/B16/P2048/append": {
-        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
-        "fetch_kib": 103365.854 + 601.333, "fetch_scale": 1048576 / 524315.250,
-        "write_kib": 1104.245 + 256.000, "write_scale": 1048576 / 1048576.000,
+        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
+        "fetch_kib": 103365.750 + 599.333, "fetch_scale": 1048576 / 524313.938,
+        "write_kib": 1104.167 + 256.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama7b_fp8kv/B16/P4096/append": {
-        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
-        "fetch_kib": 154699.083, "fetch_scale": 1048576 / 524308.188,
+        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
+        "fetch_kib": 154699.156, "fetch_scale": 1048576 / 524308.250,
         "write_kib": 512.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "gqa70b_fp8kv/B16/P1024/append": {
-        "sources": "1910f06c94a78e383c40c597556dbb5e54b26d6b78805b4d783c028ffb8d7441",
-        "fetch_kib": 49056.188 + 969.333, "fetch_scale": 1048576 / 524307.750,
-        "write_kib": 1824.083 + 256.000, "write_scale": 1048576 / 1048576.000,
+        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
+        "fetch_kib": 49056.198 + 1111.333, "fetch_scale": 1048576 / 524307.188,
+        "write_kib": 1824.042 + 256.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
 }
 
@@ -339,20 +339,40 @@ class ReadProbe:
             best = min(best, e0.elapsed_time(e1) / 1e3)
         return buf.numel() * 4 / best / 1e9
 
-    def same_bytes(self, kv_bytes: int, tile: int) -> float:
-        torch = self.torch
+    def same_bytes(self, kv_bytes: int, tile: int, calls: int = 12) -> float:
+        """Mean rate of ``calls`` cold reads of ``kv_bytes`` as random tiles.
+
+        Each call reads the next slice of the 2 GiB buffer, so that (like the
+        timed decode steps, which rotate pool copies) no call finds its bytes
+        in the last-level cache: re-reading one 100 MB slice measured ~25%
+        faster than reading it cold."""
+        torch, pa = self.torch, self.pa
         n = max(1, min(kv_bytes // tile, self.big.numel() * 4 // tile))
         perm = torch.randperm(n, device="cuda",
                               generator=torch.Generator(device="cuda").manual_seed(1)).int()
-        return self.best_gbps(self.big[:n * tile // 4], tile, perm)
+        words = n * tile // 4
+        slices = self.big.numel() // words
+        stream = torch.cuda.current_stream()
+        pa.pa_read_probe(self.big[:words], tile, perm, self.sink)
+        total = 0.0
+        for i in range(1, calls + 1):
+            k = i % slices
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pa.pa_read_probe(self.big[k * words:(k + 1) * words], tile, perm, self.sink)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1) / 1e3
+        return n * tile * calls / total / 1e9
 
     def full(self, kv_bytes: int, tile: int) -> dict:
         torch = self.torch
         perm = torch.randperm(self.big.numel() * 4 // 4096, device="cuda",
                               generator=torch.Generator(device="cuda").manual_seed(0)).int()
         return {"how": "pa_read_probe, best of 5 HIP-event-timed calls: 2 GiB in index "
-                       "order, 2 GiB as random 4 KB tiles, the call's K+V bytes as its own "
-                       "tiles in random order",
+                       "order, 2 GiB as random 4 KB tiles; the call's K+V bytes as its own "
+                       "tiles in random order, mean of 12 calls that each read another slice "
+                       "of the 2 GiB (cold in the last-level cache, as the decode steps are)",
                 "same_bytes_tile_bytes": tile,
                 "contiguous_gbps": self.best_gbps(self.big, 4096, None),
                 "random_4k_tiles_gbps": self.best_gbps(self.big, 4096, perm),
@@ -768,8 +788,14 @@ def bench_cache_write(args) -> dict:
     key = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
     val = torch.empty_like(key).normal_(generator=g)
     rnd = torch.randperm(NB * B, device="cuda", generator=g)[:T].to(torch.int64)
+    # Through block tables: each prompt of 2048 tokens fills 128 random
+    # blocks in order (token t of a prompt at table[t // B] * B + t % B).
+    tables = torch.randperm(NB, device="cuda", generator=g)[:T // B].to(torch.int64)
+    tok = torch.arange(T, dtype=torch.int64, device="cuda")
+    by_table = tables[tok // B] * B + tok % B
     for name, slots in (("sorted_random_slots", torch.sort(rnd).values),
-                        ("consecutive_slots", torch.arange(T, dtype=torch.int64, device="cuda"))):
+                        ("block_table_slots", by_table),
+                        ("consecutive_slots", tok)):
         for _ in range(args.warmup):
             pa.pa_cache_write(key, val, kc, vc, slots)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

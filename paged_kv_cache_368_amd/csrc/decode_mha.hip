@@ -419,8 +419,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
 // Wave w takes partitions w, w + 4, ... in batches of kMergeBatch whose loads
 // are all issued before any is used, keeping its own running (max, sum,
 // output) with the same rescaling as the decode loop; the four waves are
-// combined through LDS.  Sequences that fit one partition were written
-// directly by the decode kernel and are skipped.
+// combined through LDS.  The first batch is loaded together with the
+// context length, before the sequence's partition count is known (clamped
+// to the launch's partition count, so every load stays in the workspace;
+// partitions past the sequence's count are never used).  Sequences that fit
+// one partition were written directly by the decode kernel and are skipped.
 constexpr int kMergeWaves = 4;
 constexpr int kMergeBatch = 8;
 
@@ -433,28 +436,32 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int item = blockIdx.x;                 // s * H + h
   const int s = item / a.num_heads;
-  const int ctx = a.context_lens[s];
-  const int P = a.partition_size;
-  if (ctx < 0 || ctx > a.max_context_len || ctx > a.max_blocks_per_seq * a.block_size) return;
-  const int nps = (ctx + P - 1) / P;
-  if (nps <= 1) return;                        // uniform over the work-group
-
   const size_t base = (size_t)item * a.num_partitions;
-  float m = kNegInf, l = 0.f;
-  float o[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  for (int p0 = wave; p0 < nps; p0 += kMergeWaves * kMergeBatch) {
-    float mp[kMergeBatch], lp[kMergeBatch], op[kMergeBatch][PER];
+  float mp[kMergeBatch], lp[kMergeBatch], op[kMergeBatch][PER];
+  auto load = [&](int p0, int plast) {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const int p = min(p0 + u * kMergeWaves, nps - 1);   // clamped loads are never used
+      const int p = min(p0 + u * kMergeWaves, plast);   // clamped loads are never used
       mp[u] = a.ws_ml[2 * (base + p)];
       lp[u] = a.ws_ml[2 * (base + p) + 1];
       const float *src = a.ws_o + (base + p) * D + lane * PER;
 #pragma unroll
       for (int i = 0; i < PER; ++i) op[u][i] = src[i];
     }
+  };
+  const int ctx = a.context_lens[s];
+  load(wave, a.num_partitions - 1);
+  const int P = a.partition_size;
+  if (ctx < 0 || ctx > a.max_context_len || ctx > a.max_blocks_per_seq * a.block_size) return;
+  const int nps = (ctx + P - 1) / P;
+  if (nps <= 1) return;                        // uniform over the work-group
+
+  float m = kNegInf, l = 0.f;
+  float o[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  for (int p0 = wave; p0 < nps; p0 += kMergeWaves * kMergeBatch) {
+    if (p0 != wave) load(p0, nps - 1);
     float mb = m;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
