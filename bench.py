@@ -62,49 +62,49 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
     "longctx_prefix_f16/B64/P512/append": {
-        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
-        "fetch_kib": 1984879.240 + 4257.667, "fetch_scale": 1048576 / 524316.625,
+        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
+        "fetch_kib": 1984672.427 + 4257.500, "fetch_scale": 1048576 / 524316.062,
         "write_kib": 9344.000 + 64.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "tiny_f32/B16/P256/append": {
-        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
-        "fetch_kib": 901.333, "fetch_scale": 1048576 / 524307.938,
+        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
+        "fetch_kib": 901.333, "fetch_scale": 1048576 / 524305.750,
         "write_kib": 24.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama7b_f16/B16/P4096/append": {
-        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
-        "fetch_kib": 328573.740, "fetch_scale": 1048576 / 524307.375,
+        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
+        "fetch_kib": 328579.427, "fetch_scale": 1048576 / 524307.625,
         "write_kib": 768.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B16/P4096/append": {
-        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
-        "fetch_kib": 1311896.458, "fetch_scale": 1048576 / 524314.875,
+        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
+        "fetch_kib": 1311897.281, "fetch_scale": 1048576 / 524313.312,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B32/P4096/append": {
-        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
-        "fetch_kib": 1311832.521, "fetch_scale": 1048576 / 524307.500,
+        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
+        "fetch_kib": 1311832.500, "fetch_scale": 1048576 / 524307.125,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B64/P4096/append": {
-        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
-        "fetch_kib": 1311800.135, "fetch_scale": 1048576 / 524307.750,
+        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
+        "fetch_kib": 1311800.594, "fetch_scale": 1048576 / 524307.312,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "gqa70b_bf16/B16/P2048/append": {
-        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
-        "fetch_kib": 103365.750 + 599.333, "fetch_scale": 1048576 / 524313.938,
-        "write_kib": 1104.167 + 256.000, "write_scale": 1048576 / 1048576.000,
+        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
+        "fetch_kib": 103365.833 + 601.156, "fetch_scale": 1048576 / 524313.875,
+        "write_kib": 1104.229 + 256.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama7b_fp8kv/B16/P4096/append": {
-        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
-        "fetch_kib": 154699.156, "fetch_scale": 1048576 / 524308.250,
+        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
+        "fetch_kib": 154691.135, "fetch_scale": 1048576 / 524307.375,
         "write_kib": 512.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "gqa70b_fp8kv/B16/P1024/append": {
-        "sources": "08b7f6d02cfd250c46e2eb6cc09dc98b3be67630c117a0fc508be270bbc02ccd",
-        "fetch_kib": 49056.198 + 1111.333, "fetch_scale": 1048576 / 524307.188,
-        "write_kib": 1824.042 + 256.000, "write_scale": 1048576 / 1048576.000,
+        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
+        "fetch_kib": 49056.167 + 969.135, "fetch_scale": 1048576 / 524306.938,
+        "write_kib": 1824.062 + 256.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
 }
 

@@ -413,12 +413,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   }
 }
 
-// Log-sum-exp merge of split-context partitions: one work-group of four
-// waves per (s, h).
+// Log-sum-exp merge of split-context partitions: one work-group of NW waves
+// per (s, h): one wave when the launch has at most kMergeBatch partitions
+// (its one batch of loads is the whole merge, combined in registers), four
+// otherwise.
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
-// Wave w takes partitions w, w + 4, ... in batches of kMergeBatch whose loads
+// Wave w takes partitions w, w + NW, ... in batches of kMergeBatch whose loads
 // are all issued before any is used, keeping its own running (max, sum,
-// output) with the same rescaling as the decode loop; the four waves are
+// output) with the same rescaling as the decode loop; several waves are
 // combined through LDS.  The first batch is loaded together with the
 // context length, before the sequence's partition count is known (clamped
 // to the launch's partition count, so every load stays in the workspace;
@@ -427,11 +429,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
 constexpr int kMergeWaves = 4;
 constexpr int kMergeBatch = 8;
 
-template <int DT, int D>
-__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(DecodeArgs a) {
+template <int DT, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;                  // output elements per lane
-  __shared__ float s_o[kMergeWaves][D];
-  __shared__ float s_m[kMergeWaves], s_l[kMergeWaves];
+  __shared__ float s_o[NW][D];
+  __shared__ float s_m[NW], s_l[NW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int item = blockIdx.x;                 // s * H + h
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(DecodeArgs a) {
   auto load = [&](int p0, int plast) {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const int p = min(p0 + u * kMergeWaves, plast);   // clamped loads are never used
+      const int p = min(p0 + u * NW, plast);   // clamped loads are never used
       mp[u] = a.ws_ml[2 * (base + p)];
       lp[u] = a.ws_ml[2 * (base + p) + 1];
       const float *src = a.ws_o + (base + p) * D + lane * PER;
@@ -460,12 +462,12 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(DecodeArgs a) {
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  for (int p0 = wave; p0 < nps; p0 += kMergeWaves * kMergeBatch) {
+  for (int p0 = wave; p0 < nps; p0 += NW * kMergeBatch) {
     if (p0 != wave) load(p0, nps - 1);
     float mb = m;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-      if (p0 + u * kMergeWaves < nps) mb = fmaxf(mb, mp[u]);
+      if (p0 + u * NW < nps) mb = fmaxf(mb, mp[u]);
     const float ms = mb == kNegInf ? 0.f : mb;
     const float c = exp2_fast(m - ms);
     l *= c;
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(DecodeArgs a) {
     for (int i = 0; i < PER; ++i) o[i] *= c;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      if (p0 + u * kMergeWaves < nps) {
+      if (p0 + u * NW < nps) {
         const float f = exp2_fast(mp[u] - ms);
         l = __builtin_fmaf(f, lp[u], l);
 #pragma unroll
@@ -481,6 +483,15 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(DecodeArgs a) {
       }
     }
     m = mb;
+  }
+  if constexpr (NW == 1) {
+    // One wave: its running (max, sum, output) is the merge.
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const float r = l == 0.f ? 0.f : o[i] / l;   // NaN (a poisoned partition) propagates
+      store_out<DT>(a.out, (size_t)item * D + lane * PER + i, &r, 1);
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) s_o[wave][lane * PER + i] = o[i];
@@ -493,11 +504,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(DecodeArgs a) {
     const int d = threadIdx.x;
     float Mw = s_m[0];
 #pragma unroll
-    for (int w = 1; w < kMergeWaves; ++w) Mw = fmaxf(Mw, s_m[w]);
+    for (int w = 1; w < NW; ++w) Mw = fmaxf(Mw, s_m[w]);
     const float Ms = Mw == kNegInf ? 0.f : Mw;
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = exp2_fast(s_m[w] - Ms);
       L += f * s_l[w];
       O += f * s_o[w][d];
@@ -531,7 +542,11 @@ template <int DT, int D>
 hipError_t launch_merge_t(const DecodeArgs &a, hipStream_t stream) {
   const long n = (long)a.num_seqs * a.num_heads;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3((unsigned)n), dim3(kMergeWaves * 64), 0, stream, a);
+  if (a.num_partitions <= kMergeBatch)
+    hipLaunchKernelGGL((merge_kernel<DT, D, 1>), dim3((unsigned)n), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<DT, D, kMergeWaves>), dim3((unsigned)n),
+                       dim3(kMergeWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
