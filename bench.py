@@ -179,7 +179,7 @@ def measured_traffic(workload: str, block_size: int, partition_size: int, fused:
 # ---------------------------------------------------------------------------
 
 _ORACLE_STATE = {}          # what the forked workers read (set before the fork)
-MAX_HOST_WORKERS = 16       # a one-GPU machine's share of its host's cores
+MAX_HOST_WORKERS = 16       # a one-GPU machine's share of a multi-GPU host's cores
 
 
 def host_workers() -> tuple[int, int]:
@@ -922,7 +922,7 @@ def bench_prefill(args) -> dict:
     torch.cuda.synchronize()
     # Warm-up: the requested calls, and then more until PREFILL_WARM_S of them
     # have run: the matrix-core-bound launch runs at the engine clock, which
-    # rises over the first ~0.1 s of load (measured on one box: 405 us per
+    # rises over the first ~0.1 s of load (measured on one machine: 405 us per
     # call after 3 warm-up calls, 361 us after 2000; the decode launches,
     # bound by HBM, do not move).
     warm = 0
