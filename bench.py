@@ -62,49 +62,49 @@ ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 # to them reports traffic as null until the counters are taken again.
 COUNTERS = {
     "longctx_prefix_f16/B64/P512/append": {
-        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
-        "fetch_kib": 1984672.427 + 4257.500, "fetch_scale": 1048576 / 524316.062,
+        "sources": "321b93fa98b1f2d6220ac623acdd1e1e93ddd87176427f2a6f5a1e190b251427",
+        "fetch_kib": 1996293.396 + 4253.500, "fetch_scale": 1048576 / 524318.688,
         "write_kib": 9344.000 + 64.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "tiny_f32/B16/P256/append": {
-        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
-        "fetch_kib": 901.333, "fetch_scale": 1048576 / 524305.750,
+        "sources": "321b93fa98b1f2d6220ac623acdd1e1e93ddd87176427f2a6f5a1e190b251427",
+        "fetch_kib": 902.833, "fetch_scale": 1048576 / 524308.125,
         "write_kib": 24.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama7b_f16/B16/P4096/append": {
-        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
-        "fetch_kib": 328579.427, "fetch_scale": 1048576 / 524307.625,
+        "sources": "321b93fa98b1f2d6220ac623acdd1e1e93ddd87176427f2a6f5a1e190b251427",
+        "fetch_kib": 328581.667, "fetch_scale": 1048576 / 524308.062,
         "write_kib": 768.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B16/P4096/append": {
-        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
-        "fetch_kib": 1311897.281, "fetch_scale": 1048576 / 524313.312,
+        "sources": "321b93fa98b1f2d6220ac623acdd1e1e93ddd87176427f2a6f5a1e190b251427",
+        "fetch_kib": 1311891.875, "fetch_scale": 1048576 / 524313.750,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B32/P4096/append": {
-        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
-        "fetch_kib": 1311832.500, "fetch_scale": 1048576 / 524307.125,
+        "sources": "321b93fa98b1f2d6220ac623acdd1e1e93ddd87176427f2a6f5a1e190b251427",
+        "fetch_kib": 1311827.156, "fetch_scale": 1048576 / 524307.438,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama13b_bf16/B64/P4096/append": {
-        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
-        "fetch_kib": 1311800.594, "fetch_scale": 1048576 / 524307.312,
+        "sources": "321b93fa98b1f2d6220ac623acdd1e1e93ddd87176427f2a6f5a1e190b251427",
+        "fetch_kib": 1311795.740, "fetch_scale": 1048576 / 524307.375,
         "write_kib": 1920.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "gqa70b_bf16/B16/P2048/append": {
-        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
-        "fetch_kib": 103365.833 + 601.156, "fetch_scale": 1048576 / 524313.875,
-        "write_kib": 1104.229 + 256.000, "write_scale": 1048576 / 1048576.000,
+        "sources": "321b93fa98b1f2d6220ac623acdd1e1e93ddd87176427f2a6f5a1e190b251427",
+        "fetch_kib": 103365.875 + 606.333, "fetch_scale": 1048576 / 524314.875,
+        "write_kib": 1104.161 + 256.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "llama7b_fp8kv/B16/P4096/append": {
-        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
-        "fetch_kib": 154691.135, "fetch_scale": 1048576 / 524307.375,
+        "sources": "321b93fa98b1f2d6220ac623acdd1e1e93ddd87176427f2a6f5a1e190b251427",
+        "fetch_kib": 154701.083, "fetch_scale": 1048576 / 524307.938,
         "write_kib": 512.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
     "gqa70b_fp8kv/B16/P1024/append": {
-        "sources": "39fd848da87220097c8f75dda9ca51d627e1e28e20660c0f1a9755b5365790c5",
-        "fetch_kib": 49056.167 + 969.135, "fetch_scale": 1048576 / 524306.938,
-        "write_kib": 1824.062 + 256.000, "write_scale": 1048576 / 1048576.000,
+        "sources": "321b93fa98b1f2d6220ac623acdd1e1e93ddd87176427f2a6f5a1e190b251427",
+        "fetch_kib": 49056.146 + 975.333, "fetch_scale": 1048576 / 524307.375,
+        "write_kib": 1824.188 + 256.000, "write_scale": 1048576 / 1048576.000,
         "profile": "profiles/decode_counters_all_workloads.md"},
 }
 

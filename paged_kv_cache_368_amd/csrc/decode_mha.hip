@@ -8,12 +8,16 @@
 // from the physical block block_tables[s][t / B] at offset t % B (P3 §3).
 //
 // Work decomposition.  One work-group of 4 waves owns one (sequence, head,
-// partition).  The partition's slice of the block table is staged once into
-// LDS; each wave then keeps the ids of the chunks it owns in one VGPR (lane k
-// = its k-th chunk) and reads them with v_readlane, so no dependent memory
-// load sits between one chunk's K/V loads and the next.  Waves take the
-// partition's 16-token chunks round-robin, so at any moment the work-group
-// streams four neighbouring chunks.
+// partition), or R consecutive partitions of one (sequence, head) taken one
+// after the other when the context is split many ways (each still written as
+// its own partial: the context length and q are loaded once, and the next
+// partition's slice of the block table while this one streams).  The
+// partition's slice of the block table is staged once into LDS; each wave
+// then keeps the ids of the chunks it owns in one VGPR (lane k = its k-th
+// chunk) and reads them with v_readlane, so no dependent memory load sits
+// between one chunk's K/V loads and the next.  Waves take the partition's
+// 16-token chunks round-robin, so at any moment the work-group streams four
+// neighbouring chunks.
 //
 // Lane layout.  A K or V row of one token is D * elem bytes = LPT lanes x 16
 // bytes (LPT = 16 for fp16/bf16 D=128 and fp32 D=64), so one 16-byte load per
@@ -141,23 +145,26 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   const int item = group_on_xcd(blockIdx.x, gridDim.x, G);
   const int h = item % H;
   const int s = (item / H) % S;
-  const int p = item / (H * S);
+  const int pg = item / (H * S);              // partitions pg * R .. pg * R + R - 1
+  const int R = a.parts_per_group;
   const int kvh = h / G;
   const int row = lane / LPT;
   const int col = lane % LPT;
   const int P = a.partition_size;
-  const int t0 = p * P;
-  const int b0 = t0 >> a.log2_block;
   const size_t row_out = ((size_t)s * H + h) * D;
 
   // Issue the three independent prologue loads together: the context length,
-  // this partition's window of the block table (every entry the window can
+  // the first partition's window of the block table (every entry the window can
   // hold that exists in the table, whatever the context turns out to be) and
   // q, a 16-byte slice per lane (every row of the wave holds the same slice).
   const int ctx = a.context_lens[s];
-  const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks_per_seq + b0;
-  const int window = min(P >> a.log2_block, a.max_blocks_per_seq - b0);
-  const int id = tid < window ? trow[tid] : -1;
+  // Partition pp's window of the block table: entry tid, if the table has it.
+  auto table_entry = [&](int pp) -> int {
+    const int bb = (pp * P) >> a.log2_block;
+    const int window = min(P >> a.log2_block, a.max_blocks_per_seq - bb);
+    return tid < window ? a.block_tables[(size_t)s * a.max_blocks_per_seq + bb + tid] : -1;
+  };
+  int id = table_entry(pg * R);
   u32x4 qv[QW];
 #pragma unroll
   for (int i = 0; i < QW; ++i)
@@ -197,219 +204,233 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
   const bool bad_ctx = ctx < 0 || ctx > a.max_context_len ||
                        ctx > a.max_blocks_per_seq * a.block_size;
   const int nps = bad_ctx ? 1 : (ctx + P - 1) / P;
-  if (p >= (nps > 0 ? nps : 1)) return;           // uniform over the work-group
+  const int nps1 = nps > 0 ? nps : 1;
   const bool direct = nps <= 1;
-  const int t1 = bad_ctx ? t0 : min(t0 + P, ctx);
-  const int nblk = bad_ctx ? 0 : ((t1 - t0 + a.block_size - 1) >> a.log2_block);
+  // The work-group's partitions one after the other, each written as its own
+  // partial; the next one's table window is loaded before this one streams.
+  for (int rr = 0; rr < R; ++rr) {
+    const int p = pg * R + rr;
+    if (p >= nps1) break;                             // uniform over the work-group
+    const int t0 = p * P;
+    const int id_next = rr + 1 < R && p + 1 < nps1 ? table_entry(p + 1) : -1;
+    const int t1 = bad_ctx ? t0 : min(t0 + P, ctx);
+    const int nblk = bad_ctx ? 0 : ((t1 - t0 + a.block_size - 1) >> a.log2_block);
 
-  // Stage the block ids in use; flag any outside the pool.
-  const bool bad_id = tid < nblk && (id < 0 || id >= a.num_blocks);
-  if (tid < nblk) s_tbl[tid] = id;
-  const bool poison = __syncthreads_or(bad_id) || bad_ctx;
+    // Stage the block ids in use; flag any outside the pool.
+    const bool bad_id = tid < nblk && (id < 0 || id >= a.num_blocks);
+    if (tid < nblk) s_tbl[tid] = id;
+    const bool poison = __syncthreads_or(bad_id) || bad_ctx;
 
-  const size_t part = ((size_t)s * H + h) * a.num_partitions + p;
-  // The new token's slot: written by the first query head of its kv head, in
-  // the partition that holds the token (one 16-byte slice per lane of row 0).
-  const size_t head_stride = (size_t)a.block_size * D;        // elements per (block, head) tile
-  const size_t block_stride = head_stride * a.num_kv_heads;
-  // Like the separate cache write, it needs only the token's own slot to be
-  // valid (a bad id elsewhere in the table poisons the output, not the write).
-  if (append && tid < LPT && !bad_ctx && ctx > t0 && ctx <= t1 && h % G == 0) {
-    const int tn = ctx - 1;
-    const int phys = s_tbl[(tn - t0) >> a.log2_block];
-    if (phys >= 0 && phys < a.num_blocks) {
-      const size_t dst = ((size_t)phys * block_stride + kvh * head_stride +
-                          (size_t)(tn & (a.block_size - 1)) * D + col * EPL) * E;
-      *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_store) + dst) = s_new[0][col];
-      *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_store) + dst) = s_new[1][col];
-    }
-  }
-  if (poison) {
-    const float nan = __builtin_nanf("");
-    if (direct) {
-      if (tid < D) {
-        float v = nan;
-        store_out<DT>(a.out, row_out + tid, &v, 1);
-      }
-    } else {
-      if (tid < D) store_partial(a.ws_o + part * D + tid, nan);
-      if (tid == 0) {
-        store_partial(a.ws_ml + 2 * part, __builtin_inff());
-        store_partial(a.ws_ml + 2 * part + 1, nan);
+    const size_t part = ((size_t)s * H + h) * a.num_partitions + p;
+    // The new token's slot: written by the first query head of its kv head, in
+    // the partition that holds the token (one 16-byte slice per lane of row 0).
+    const size_t head_stride = (size_t)a.block_size * D;        // elements per (block, head) tile
+    const size_t block_stride = head_stride * a.num_kv_heads;
+    // Like the separate cache write, it needs only the token's own slot to be
+    // valid (a bad id elsewhere in the table poisons the output, not the write).
+    if (append && tid < LPT && !bad_ctx && ctx > t0 && ctx <= t1 && h % G == 0) {
+      const int tn = ctx - 1;
+      const int phys = s_tbl[(tn - t0) >> a.log2_block];
+      if (phys >= 0 && phys < a.num_blocks) {
+        const size_t dst = ((size_t)phys * block_stride + kvh * head_stride +
+                            (size_t)(tn & (a.block_size - 1)) * D + col * EPL) * E;
+        *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_store) + dst) = s_new[0][col];
+        *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_store) + dst) = s_new[1][col];
       }
     }
-    return;
-  }
-
-  // Tokens read from the pool: [t0, tp); the newest token, when appending,
-  // comes from LDS instead.
-  const bool holds_new = append && ctx > t0 && ctx <= t1;        // uniform
-  const int tp = holds_new ? ctx - 1 : t1;
-  const int nch = (tp - t0 + kChunk - 1) / kChunk;
-  const int nch_w = nch > wave ? (nch - wave + NW - 1) / NW : 0;
-  // This wave's chunk k is partition chunk wave + NW*k; lane k keeps its block id.
-  int my_ids = 0;
-  if (lane < nch_w) my_ids = s_tbl[((wave + NW * lane) * kChunk) >> a.log2_block];
-
-  const char *kbase =
-      scalar_ptr(reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E);
-  const char *vbase =
-      scalar_ptr(reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E);
-  const int lane_off = (row * D + col * EPL) * E;
-
-  // Byte offset (from the kv head's first tile) of this wave's chunk k.
-  auto chunk_offset = [&](int k) -> size_t {
-    const int phys = __builtin_amdgcn_readlane(my_ids, k);
-    const int tok = (wave + NW * k) * kChunk;                 // relative to t0, block aligned
-    const int off = tok & (a.block_size - 1);
-    return ((size_t)phys * block_stride + (size_t)off * D) * E;
-  };
-
-  // K and V of one chunk are read through two buffer descriptors whose base
-  // is the chunk's first row (scalar registers) and whose range is the chunk:
-  // every lane then needs only its 32-bit offset, and nothing outside the
-  // chunk can be touched.
-  constexpr int kChunkBytes = kChunk * D * E;
-  // Chunks past the wave's last one (the pipeline's run-out) are loaded
-  // through an empty descriptor: such loads return zeros without touching
-  // memory, and their registers are never consumed.
-  auto load = [&](u32x4 *kb, u32x4 *vb, int k, int last) {
-    const size_t off = chunk_offset(min(k, last));
-    const int range = k <= last ? kChunkBytes : 0;
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, range, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, range, kBufferFlags);
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-      kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + j * TPL * D * E, 0, kStreamPolicy);
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-      vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + j * TPL * D * E, 0, kStreamPolicy);
-    // Keep the scheduler from sinking these loads below the compute that
-    // follows: they must be in flight while the previous chunk is consumed.
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  float m = kNegInf, l = 0.f;
-  float o[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) o[i] = 0.f;
-
-  // One 16-token chunk starting at token tc; rows at or past tend are masked.
-  auto consume = [&](const u32x4 *kb, const u32x4 *vb, int tc, int tend) {
-    float sc[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) sc[j] = group_sum<LPT>(lane_dot<DT, KT>(qv, kb[j])) * a.scale_log2;
-    const bool tail = tc + kChunk > tend;                     // last chunk: mask past the context
-    bool valid[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      valid[j] = !tail || (tc + j * TPL + row < tend);
-      sc[j] = valid[j] ? sc[j] : kNegInf;
+    if (poison) {
+      const float nan = __builtin_nanf("");
+      if (direct) {
+        if (tid < D) {
+          float v = nan;
+          store_out<DT>(a.out, row_out + tid, &v, 1);
+        }
+      } else {
+        if (tid < D) store_partial(a.ws_o + part * D + tid, nan);
+        if (tid == 0) {
+          store_partial(a.ws_ml + 2 * part, __builtin_inff());
+          store_partial(a.ws_ml + 2 * part + 1, nan);
+        }
+      }
+      __syncthreads();                              // s_tbl is rewritten next
+      id = id_next;
+      continue;
     }
-    float mloc = sc[0];
-#pragma unroll
-    for (int j = 1; j < NL; ++j) mloc = fmaxf(mloc, sc[j]);
-    const float mnew = fmaxf(m, mloc);
-    const float msafe = mnew == kNegInf ? 0.f : mnew;
-    const float corr = exp2_fast(m - msafe);
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) o[i] *= corr;
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const float pj = exp2_fast(sc[j] - msafe);
-      psum += pj;
-      const u32x4 v = valid[j] ? vb[j] : u32x4{0u, 0u, 0u, 0u};
-      lane_axpy<KT>(o, pj, v);
-    }
-    l = l * corr + psum;
-    m = mnew;
-  };
 
-  // Software pipeline over NBUF register buffers: while chunk k is consumed,
-  // chunks k+1 .. k+NBUF-1 are in flight.  Loads past the last chunk go
-  // through an empty descriptor (see load).
-  constexpr int NBUF = KT == kFP8 ? kDecodeBuffersFp8 : kDecodeBuffers;
-  u32x4 kb[NBUF][NL], vb[NBUF][NL];
-  if (nch_w > 0) {
-    const int last = nch_w - 1;
+    // Tokens read from the pool: [t0, tp); the newest token, when appending,
+    // comes from LDS instead.
+    const bool holds_new = append && ctx > t0 && ctx <= t1;        // uniform
+    const int tp = holds_new ? ctx - 1 : t1;
+    const int nch = (tp - t0 + kChunk - 1) / kChunk;
+    const int nch_w = nch > wave ? (nch - wave + NW - 1) / NW : 0;
+    // This wave's chunk k is partition chunk wave + NW*k; lane k keeps its block id.
+    int my_ids = 0;
+    if (lane < nch_w) my_ids = s_tbl[((wave + NW * lane) * kChunk) >> a.log2_block];
+
+    const char *kbase =
+        scalar_ptr(reinterpret_cast<const char *>(a.k_cache) + kvh * head_stride * E);
+    const char *vbase =
+        scalar_ptr(reinterpret_cast<const char *>(a.v_cache) + kvh * head_stride * E);
+    const int lane_off = (row * D + col * EPL) * E;
+
+    // Byte offset (from the kv head's first tile) of this wave's chunk k.
+    auto chunk_offset = [&](int k) -> size_t {
+      const int phys = __builtin_amdgcn_readlane(my_ids, k);
+      const int tok = (wave + NW * k) * kChunk;                 // relative to t0, block aligned
+      const int off = tok & (a.block_size - 1);
+      return ((size_t)phys * block_stride + (size_t)off * D) * E;
+    };
+
+    // K and V of one chunk are read through two buffer descriptors whose base
+    // is the chunk's first row (scalar registers) and whose range is the chunk:
+    // every lane then needs only its 32-bit offset, and nothing outside the
+    // chunk can be touched.
+    constexpr int kChunkBytes = kChunk * D * E;
+    // Chunks past the wave's last one (the pipeline's run-out) are loaded
+    // through an empty descriptor: such loads return zeros without touching
+    // memory, and their registers are never consumed.
+    auto load = [&](u32x4 *kb, u32x4 *vb, int k, int last) {
+      const size_t off = chunk_offset(min(k, last));
+      const int range = k <= last ? kChunkBytes : 0;
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, range, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, range, kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) load(kb[i], vb[i], i, last);
-    for (int k0 = 0; k0 < nch_w; k0 += NBUF) {
+      for (int j = 0; j < NL; ++j)
+        kb[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + j * TPL * D * E, 0,
+                                                       kStreamPolicy);
 #pragma unroll
-      for (int i = 0; i < NBUF; ++i) {
-        const int k = k0 + i;
-        if (k >= nch_w) break;
-        load(kb[(i + NBUF - 1) % NBUF], vb[(i + NBUF - 1) % NBUF], k + NBUF - 1, last);
-        consume(kb[i], vb[i], t0 + (wave + NW * k) * kChunk, tp);
+      for (int j = 0; j < NL; ++j)
+        vb[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + j * TPL * D * E, 0,
+                                                       kStreamPolicy);
+      // Keep the scheduler from sinking these loads below the compute that
+      // follows: they must be in flight while the previous chunk is consumed.
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    float m = kNegInf, l = 0.f;
+    float o[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] = 0.f;
+
+    // One 16-token chunk starting at token tc; rows at or past tend are masked.
+    auto consume = [&](const u32x4 *kb, const u32x4 *vb, int tc, int tend) {
+      float sc[NL];
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+        sc[j] = group_sum<LPT>(lane_dot<DT, KT>(qv, kb[j])) * a.scale_log2;
+      const bool tail = tc + kChunk > tend;                     // last chunk: mask past the context
+      bool valid[NL];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        valid[j] = !tail || (tc + j * TPL + row < tend);
+        sc[j] = valid[j] ? sc[j] : kNegInf;
+      }
+      float mloc = sc[0];
+#pragma unroll
+      for (int j = 1; j < NL; ++j) mloc = fmaxf(mloc, sc[j]);
+      const float mnew = fmaxf(m, mloc);
+      const float msafe = mnew == kNegInf ? 0.f : mnew;
+      const float corr = exp2_fast(m - msafe);
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) o[i] *= corr;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const float pj = exp2_fast(sc[j] - msafe);
+        psum += pj;
+        const u32x4 v = valid[j] ? vb[j] : u32x4{0u, 0u, 0u, 0u};
+        lane_axpy<KT>(o, pj, v);
+      }
+      l = l * corr + psum;
+      m = mnew;
+    };
+
+    // Software pipeline over NBUF register buffers: while chunk k is consumed,
+    // chunks k+1 .. k+NBUF-1 are in flight.  Loads past the last chunk go
+    // through an empty descriptor (see load).
+    constexpr int NBUF = KT == kFP8 ? kDecodeBuffersFp8 : kDecodeBuffers;
+    u32x4 kb[NBUF][NL], vb[NBUF][NL];
+    if (nch_w > 0) {
+      const int last = nch_w - 1;
+#pragma unroll
+      for (int i = 0; i < NBUF - 1; ++i) load(kb[i], vb[i], i, last);
+      for (int k0 = 0; k0 < nch_w; k0 += NBUF) {
+#pragma unroll
+        for (int i = 0; i < NBUF; ++i) {
+          const int k = k0 + i;
+          if (k >= nch_w) break;
+          load(kb[(i + NBUF - 1) % NBUF], vb[(i + NBUF - 1) % NBUF], k + NBUF - 1, last);
+          consume(kb[i], vb[i], t0 + (wave + NW * k) * kChunk, tp);
+        }
       }
     }
-  }
-  // The newest token as a chunk of one valid row (row 0 of wave 0).
-  if (holds_new && wave == 0) {
-    u32x4 kn[NL], vn[NL];
+    // The newest token as a chunk of one valid row (row 0 of wave 0).
+    if (holds_new && wave == 0) {
+      u32x4 kn[NL], vn[NL];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const bool mine = j == 0 && row == 0;
-      kn[j] = mine ? s_new[0][col] : u32x4{0u, 0u, 0u, 0u};
-      vn[j] = mine ? s_new[1][col] : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < NL; ++j) {
+        const bool mine = j == 0 && row == 0;
+        kn[j] = mine ? s_new[0][col] : u32x4{0u, 0u, 0u, 0u};
+        vn[j] = mine ? s_new[1][col] : u32x4{0u, 0u, 0u, 0u};
+      }
+      consume(kn, vn, ctx - 1, ctx);
     }
-    consume(kn, vn, ctx - 1, ctx);
-  }
 
-  // Merge the rows of this wave (lanes with equal col, different row).
-  float M = m;
+    // Merge the rows of this wave (lanes with equal col, different row).
+    float M = m;
 #pragma unroll
-  for (int msk = LPT; msk < 64; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk));
-  {
-    const float Ms = M == kNegInf ? 0.f : M;
-    const float w = exp2_fast(m - Ms);
-    l *= w;
+    for (int msk = LPT; msk < 64; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk));
+    {
+      const float Ms = M == kNegInf ? 0.f : M;
+      const float w = exp2_fast(m - Ms);
+      l *= w;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) o[i] *= w;
-  }
-#pragma unroll
-  for (int msk = LPT; msk < 64; msk <<= 1) {
-    l += __shfl_xor(l, msk);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) o[i] += __shfl_xor(o[i], msk);
-  }
-  if (row == 0) {
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) s_o[wave][col * EPL + i] = o[i];
-    if (col == 0) {
-      s_m[wave] = M;
-      s_l[wave] = l;
+      for (int i = 0; i < EPL; ++i) o[i] *= w;
     }
-  }
-  __syncthreads();
-
-  // Merge the NW waves; thread d < D owns output element d.
-  if (tid < D) {
-    float Mw = s_m[0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) Mw = fmaxf(Mw, s_m[w]);
-    const float Ms = Mw == kNegInf ? 0.f : Mw;
-    float L = 0.f, O = 0.f;
+    for (int msk = LPT; msk < 64; msk <<= 1) {
+      l += __shfl_xor(l, msk);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = exp2_fast(s_m[w] - Ms);
-      L += f * s_l[w];
-      O += f * s_o[w][tid];
+      for (int i = 0; i < EPL; ++i) o[i] += __shfl_xor(o[i], msk);
     }
-    if constexpr (KT == kFP8) O *= a.v_scale;   // values are code * V pool scale
-    if (direct) {
-      const float r = L == 0.f ? 0.f : O / L;   // NaN (a poisoned partition) propagates
-      store_out<DT>(a.out, row_out + tid, &r, 1);
-    } else {
-      store_partial(a.ws_o + part * D + tid, O);
-      if (tid == 0) {
-        store_partial(a.ws_ml + 2 * part, Mw);
-        store_partial(a.ws_ml + 2 * part + 1, L);
+    if (row == 0) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) s_o[wave][col * EPL + i] = o[i];
+      if (col == 0) {
+        s_m[wave] = M;
+        s_l[wave] = l;
       }
     }
+    __syncthreads();
+
+    // Merge the NW waves; thread d < D owns output element d.
+    if (tid < D) {
+      float Mw = s_m[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) Mw = fmaxf(Mw, s_m[w]);
+      const float Ms = Mw == kNegInf ? 0.f : Mw;
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = exp2_fast(s_m[w] - Ms);
+        L += f * s_l[w];
+        O += f * s_o[w][tid];
+      }
+      if constexpr (KT == kFP8) O *= a.v_scale;   // values are code * V pool scale
+      if (direct) {
+        const float r = L == 0.f ? 0.f : O / L;   // NaN (a poisoned partition) propagates
+        store_out<DT>(a.out, row_out + tid, &r, 1);
+      } else {
+        store_partial(a.ws_o + part * D + tid, O);
+        if (tid == 0) {
+          store_partial(a.ws_ml + 2 * part, Mw);
+          store_partial(a.ws_ml + 2 * part + 1, L);
+        }
+      }
+    }
+    id = id_next;
   }
 }
 
@@ -518,12 +539,24 @@ __global__ __launch_bounds__(NW * 64) void merge_kernel(DecodeArgs a) {
   }
 }
 
+// Partitions per vector work-group: four when the context is split at least
+// eight ways and that still leaves 4096 work-groups (four rounds of the
+// 1024 that 256 CUs hold at once), else one.  On 8 sequences x 32 heads of
+// 64 partitions: 639-641 against 642-644 us per call.
+inline int mha_parts_per_group(long items, int np) {
+  constexpr int R = 4;
+  return np >= 2 * R && items * ((np + R - 1) / R) >= 4096 ? R : 1;
+}
+
 template <int DT, int KT, int D>
 hipError_t launch_mha_kt(const DecodeArgs &a, hipStream_t stream) {
-  const long n = (long)a.num_seqs * a.num_heads * a.num_partitions;
+  DecodeArgs b = a;
+  b.parts_per_group = mha_parts_per_group((long)a.num_seqs * a.num_heads, a.num_partitions);
+  const long groups = (a.num_partitions + b.parts_per_group - 1) / b.parts_per_group;
+  const long n = (long)a.num_seqs * a.num_heads * groups;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL((decode_mha_kernel<DT, KT, D, kDecodeWaves>), dim3((unsigned)n),
-                     dim3(kDecodeWaves * 64), 0, stream, a);
+                     dim3(kDecodeWaves * 64), 0, stream, b);
   return hipGetLastError();
 }
 

@@ -50,6 +50,7 @@ struct DecodeArgs {
   float v_scale;             // the V pool scale for fp8 pools (1 otherwise)
   int partition_size;        // P
   int num_partitions;        // NP = ceil(max_context_len / P), >= 1
+  int parts_per_group;       // consecutive partitions per vector work-group (set by its launch)
   // Appending decode (null otherwise): token context_lens[s] - 1 of every
   // sequence is new; its K/V rows [S][Hkv][D] are attended from here and
   // written to the token's slot in the pools (k_store/v_store: the pools).
